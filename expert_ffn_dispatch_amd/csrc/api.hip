@@ -1,0 +1,389 @@
+// C ABI of the MoE FFN layer: argument checks, workspace carving and the
+// launch sequence.  Every check runs on the host before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/moe_ffn.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local hipEvent_t g_stage_ev[MOE_STAGE_EVENTS];
+thread_local bool g_stage_on = false;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+int device_error(const char* where, hipError_t e) {
+  return fail(MOE_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQ_PTR(p)                                                                        \
+  do {                                                                                    \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID, "%s: %s is NULL", fn, #p);          \
+    if (!aligned(p)) return fail(MOE_ERR_INVALID, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+#define OPT_PTR(p)                                                                        \
+  do {                                                                                    \
+    if ((p) != nullptr && !aligned(p))                                                    \
+      return fail(MOE_ERR_INVALID, "%s: %s is not 16-byte aligned", fn, #p);             \
+  } while (0)
+
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 16;
+
+// Shape limits shared by every entry point.  `need_k`: top_k must be valid.
+int check_dims(const char* fn, const moe_dims* d, bool need_router_shape) {
+  if (d == nullptr) return fail(MOE_ERR_INVALID, "%s: dims is NULL", fn);
+  if (d->n_tokens < 1 || d->n_tokens > (1 << 20))
+    return fail(MOE_ERR_INVALID, "%s: n_tokens=%d outside [1, 2^20]", fn, d->n_tokens);
+  if (d->hidden < 64 || d->hidden > 16384 || d->hidden % 64 != 0)
+    return fail(MOE_ERR_INVALID, "%s: hidden=%d must be a multiple of 64 in [64, 16384]", fn, d->hidden);
+  if (d->n_experts < 1)
+    return fail(MOE_ERR_INVALID, "%s: n_experts=%d must be >= 1", fn, d->n_experts);
+  if (d->n_experts > kMaxE)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: n_experts=%d above the supported %d", fn, d->n_experts, kMaxE);
+  if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > kMaxK)
+    return fail(MOE_ERR_INVALID, "%s: top_k=%d must be in [1, min(n_experts, %d)]", fn, d->top_k, kMaxK);
+  if ((long long)d->n_tokens * d->top_k > (1 << 24))
+    return fail(MOE_ERR_INVALID, "%s: n_tokens*top_k above 2^24", fn);
+  if (need_router_shape) {
+    if (d->expert_width < 64 || d->expert_width > 65536 || d->expert_width % 64 != 0)
+      return fail(MOE_ERR_INVALID, "%s: expert_width=%d must be a multiple of 64 in [64, 65536]", fn,
+                  d->expert_width);
+    if (d->n_shared < 0) return fail(MOE_ERR_INVALID, "%s: n_shared=%d < 0", fn, d->n_shared);
+    if (d->n_shared > 0) {
+      const long long sh = (long long)d->n_shared * d->shared_width;
+      if (d->shared_width < 1 || sh > 65536 || sh % 64 != 0)
+        return fail(MOE_ERR_INVALID,
+                    "%s: n_shared*shared_width=%lld must be a positive multiple of 64 <= 65536", fn, sh);
+    }
+  }
+  return MOE_OK;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t n) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(n * sizeof(T));
+    return p;
+  }
+};
+
+struct PermuteWs {
+  int32_t* tile_hist;
+  int32_t* tile_off;
+};
+PermuteWs carve_permute(Carver& c, int A, int E) {
+  const size_t T = (size_t)moe::ceil_div(A, moe::kPermTile);
+  PermuteWs w;
+  w.tile_hist = c.take<int32_t>((size_t)E * T);
+  w.tile_off = c.take<int32_t>((size_t)E * T);
+  return w;
+}
+
+struct LayerWs {
+  int32_t* ids;
+  float* wts;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* s2a;
+  int32_t* a2s;
+  int32_t* row_token;
+  float* row_weight;
+  PermuteWs perm;
+  uint16_t* h;
+  uint16_t* y;
+  uint16_t* hs;
+  uint16_t* ys;
+};
+LayerWs carve_layer(Carver& c, const moe_dims& d) {
+  const size_t N = d.n_tokens, A = (size_t)d.n_tokens * d.top_k, E = d.n_experts;
+  const size_t SH = (size_t)d.n_shared * (d.n_shared > 0 ? d.shared_width : 0);
+  LayerWs w;
+  w.ids = c.take<int32_t>(A);
+  w.wts = c.take<float>(A);
+  w.counts = c.take<int32_t>(E);
+  w.offsets = c.take<int32_t>(E + 1);
+  w.s2a = c.take<int32_t>(A);
+  w.a2s = c.take<int32_t>(A);
+  w.row_token = c.take<int32_t>(A);
+  w.row_weight = c.take<float>(A);
+  w.perm = carve_permute(c, (int)A, (int)E);
+  w.h = c.take<uint16_t>(A * d.expert_width);
+  w.y = c.take<uint16_t>(A * d.hidden);
+  w.hs = SH ? c.take<uint16_t>(N * SH) : nullptr;
+  w.ys = SH ? c.take<uint16_t>(N * d.hidden) : nullptr;
+  return w;
+}
+
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      return -1;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+int check_ws(const char* fn, void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (ws == nullptr) return fail(MOE_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_set_stage_events(void* const* events, int n) {
+  const char* fn = "moe_set_stage_events";
+  if (events == nullptr) {
+    g_stage_on = false;
+    return ok();
+  }
+  if (n != MOE_STAGE_EVENTS) return fail(MOE_ERR_INVALID, "%s: n=%d, expected %d", fn, n, MOE_STAGE_EVENTS);
+  for (int i = 0; i < n; ++i) {
+    if (events[i] == nullptr) return fail(MOE_ERR_INVALID, "%s: events[%d] is NULL", fn, i);
+    g_stage_ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_stage_on = true;
+  return ok();
+}
+
+int moe_layer_workspace_bytes(const moe_dims* dims, uint32_t flags, size_t* bytes) {
+  const char* fn = "moe_layer_workspace_bytes";
+  if (int r = check_dims(fn, dims, true)) return r;
+  if (flags & ~uint32_t(MOE_FLAG_IDS_IN)) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID, "%s: bytes is NULL", fn);
+  Carver c(nullptr);
+  carve_layer(c, *dims);
+  *bytes = c.off;
+  return ok();
+}
+
+int moe_permute_workspace_bytes(const moe_dims* dims, size_t* bytes) {
+  const char* fn = "moe_permute_workspace_bytes";
+  if (int r = check_dims(fn, dims, false)) return r;
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID, "%s: bytes is NULL", fn);
+  Carver c(nullptr);
+  carve_permute(c, dims->n_tokens * dims->top_k, dims->n_experts);
+  *bytes = c.off;
+  return ok();
+}
+
+int moe_grouped_ffn_workspace_bytes(const moe_dims* dims, size_t* bytes) {
+  const char* fn = "moe_grouped_ffn_workspace_bytes";
+  if (int r = check_dims(fn, dims, true)) return r;
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID, "%s: bytes is NULL", fn);
+  Carver c(nullptr);
+  c.take<uint16_t>((size_t)dims->n_tokens * dims->top_k * dims->expert_width);
+  *bytes = c.off;
+  return ok();
+}
+
+int moe_route(const moe_dims* dims, const moe_bf16* x, const moe_bf16* w_router,
+              const float* router_bias, int32_t* topk_ids, float* topk_weights, moe_stream stream) {
+  const char* fn = "moe_route";
+  if (int r = check_dims(fn, dims, false)) return r;
+  REQ_PTR(x);
+  REQ_PTR(w_router);
+  OPT_PTR(router_bias);
+  REQ_PTR(topk_ids);
+  REQ_PTR(topk_weights);
+  moe::RouteArgs a{x, w_router, router_bias, dims->n_tokens, dims->hidden, dims->n_experts, dims->top_k,
+                   topk_ids, topk_weights};
+  if (hipError_t e = moe::launch_route(a, static_cast<hipStream_t>(stream))) return device_error(fn, e);
+  return ok();
+}
+
+int moe_permute(const moe_dims* dims, const int32_t* topk_ids, const moe_bf16* x, int32_t* expert_counts,
+                int32_t* expert_offsets, int32_t* sorted_to_assign, int32_t* assign_to_sorted,
+                moe_bf16* x_sorted, void* ws, size_t ws_bytes, moe_stream stream) {
+  const char* fn = "moe_permute";
+  if (int r = check_dims(fn, dims, false)) return r;
+  REQ_PTR(topk_ids);
+  REQ_PTR(expert_counts);
+  REQ_PTR(expert_offsets);
+  REQ_PTR(sorted_to_assign);
+  REQ_PTR(assign_to_sorted);
+  OPT_PTR(x_sorted);
+  if (x_sorted != nullptr) REQ_PTR(x);
+  const int A = dims->n_tokens * dims->top_k;
+  Carver sz(nullptr);
+  carve_permute(sz, A, dims->n_experts);
+  if (int r = check_ws(fn, ws, ws_bytes, sz.off)) return r;
+  Carver c(ws);
+  PermuteWs w = carve_permute(c, A, dims->n_experts);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe::PermuteArgs p{topk_ids, A, dims->n_experts, dims->top_k, expert_counts, expert_offsets,
+                     sorted_to_assign, assign_to_sorted, nullptr, nullptr, nullptr, w.tile_hist, w.tile_off};
+  if (hipError_t e = moe::launch_permute(p, st)) return device_error(fn, e);
+  if (x_sorted != nullptr) {
+    if (hipError_t e = moe::launch_gather(x, sorted_to_assign, dims->top_k, A, dims->hidden, x_sorted, st))
+      return device_error(fn, e);
+  }
+  return ok();
+}
+
+int moe_grouped_ffn(const moe_dims* dims, const moe_bf16* x_sorted, const int32_t* expert_offsets,
+                    const moe_bf16* w_gate, const moe_bf16* w_up, const moe_bf16* w_down,
+                    const float* row_scale, moe_bf16* y_sorted, void* ws, size_t ws_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn";
+  if (int r = check_dims(fn, dims, true)) return r;
+  REQ_PTR(x_sorted);
+  REQ_PTR(expert_offsets);
+  REQ_PTR(w_gate);
+  REQ_PTR(w_up);
+  REQ_PTR(w_down);
+  OPT_PTR(row_scale);
+  REQ_PTR(y_sorted);
+  size_t need = 0;
+  moe_grouped_ffn_workspace_bytes(dims, &need);
+  if (int r = check_ws(fn, ws, ws_bytes, need)) return r;
+  const int ncu = num_cus();
+  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
+  const int A = dims->n_tokens * dims->top_k;
+  uint16_t* h = static_cast<uint16_t*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe::FfnArgs g{x_sorted, nullptr, expert_offsets, 0, w_gate, w_up, nullptr, h,
+                 dims->n_experts, A, dims->hidden, dims->expert_width};
+  if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
+  moe::FfnArgs dn{h, nullptr, expert_offsets, 0, w_down, nullptr, row_scale, y_sorted,
+                  dims->n_experts, A, dims->expert_width, dims->hidden};
+  if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  return ok();
+}
+
+int moe_combine(const moe_dims* dims, const moe_bf16* y_sorted, const int32_t* assign_to_sorted,
+                const float* topk_weights, const moe_bf16* shared_out, moe_bf16* out, moe_stream stream) {
+  const char* fn = "moe_combine";
+  if (int r = check_dims(fn, dims, false)) return r;
+  REQ_PTR(y_sorted);
+  REQ_PTR(assign_to_sorted);
+  OPT_PTR(topk_weights);
+  OPT_PTR(shared_out);
+  REQ_PTR(out);
+  moe::CombineArgs a{y_sorted, assign_to_sorted, topk_weights, shared_out, out, dims->n_tokens,
+                     dims->hidden, dims->top_k};
+  if (hipError_t e = moe::launch_combine(a, static_cast<hipStream_t>(stream))) return device_error(fn, e);
+  return ok();
+}
+
+int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,
+              const float* router_bias, const moe_bf16* w_gate, const moe_bf16* w_up, const moe_bf16* w_down,
+              const moe_bf16* ws_gate, const moe_bf16* ws_up, const moe_bf16* ws_down, int32_t* topk_ids,
+              float* topk_weights, moe_bf16* out, void* ws, size_t ws_bytes, moe_stream stream) {
+  const char* fn = "moe_layer";
+  if (int r = check_dims(fn, dims, true)) return r;
+  if (flags & ~uint32_t(MOE_FLAG_IDS_IN)) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+  const bool ids_in = (flags & MOE_FLAG_IDS_IN) != 0;
+  REQ_PTR(x);
+  if (ids_in) {
+    if (w_router != nullptr || router_bias != nullptr)
+      return fail(MOE_ERR_INVALID, "%s: w_router/router_bias must be NULL with MOE_FLAG_IDS_IN", fn);
+    REQ_PTR(topk_ids);
+    REQ_PTR(topk_weights);
+  } else {
+    REQ_PTR(w_router);
+    OPT_PTR(router_bias);
+    OPT_PTR(topk_ids);
+    OPT_PTR(topk_weights);
+  }
+  REQ_PTR(w_gate);
+  REQ_PTR(w_up);
+  REQ_PTR(w_down);
+  if (dims->n_shared > 0) {
+    REQ_PTR(ws_gate);
+    REQ_PTR(ws_up);
+    REQ_PTR(ws_down);
+  } else if (ws_gate || ws_up || ws_down) {
+    return fail(MOE_ERR_INVALID, "%s: shared-expert weights given with n_shared = 0", fn);
+  }
+  REQ_PTR(out);
+  Carver sz(nullptr);
+  carve_layer(sz, *dims);
+  if (int r = check_ws(fn, ws, ws_bytes, sz.off)) return r;
+  const int ncu = num_cus();
+  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
+
+  Carver c(ws);
+  LayerWs w = carve_layer(c, *dims);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int N = dims->n_tokens, M = dims->hidden, E = dims->n_experts, k = dims->top_k, H = dims->expert_width;
+  const int A = N * k;
+  int32_t* ids = topk_ids ? topk_ids : w.ids;
+  float* wts = topk_weights ? topk_weights : w.wts;
+  const bool rec = g_stage_on;
+  g_stage_on = false;
+  auto mark = [&](int i) -> hipError_t { return rec ? hipEventRecord(g_stage_ev[i], st) : hipSuccess; };
+  if (hipError_t e = mark(0)) return device_error(fn, e);
+
+  if (!ids_in) {
+    moe::RouteArgs r{x, w_router, router_bias, N, M, E, k, ids, wts};
+    if (hipError_t e = moe::launch_route(r, st)) return device_error(fn, e);
+  }
+  if (hipError_t e = mark(1)) return device_error(fn, e);
+  moe::PermuteArgs p{ids, A, E, k, w.counts, w.offsets, w.s2a, w.a2s, w.row_token, wts, w.row_weight,
+                     w.perm.tile_hist, w.perm.tile_off};
+  if (hipError_t e = moe::launch_permute(p, st)) return device_error(fn, e);
+  if (hipError_t e = mark(2)) return device_error(fn, e);
+
+  if (dims->n_shared > 0) {
+    const int SH = dims->n_shared * dims->shared_width;
+    moe::FfnArgs g{x, nullptr, nullptr, N, ws_gate, ws_up, nullptr, w.hs, 1, N, M, SH};
+    if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
+    moe::FfnArgs dn{w.hs, nullptr, nullptr, N, ws_down, nullptr, nullptr, w.ys, 1, N, SH, M};
+    if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  }
+  if (hipError_t e = mark(3)) return device_error(fn, e);
+  moe::FfnArgs g{x, w.row_token, w.offsets, 0, w_gate, w_up, nullptr, w.h, E, A, M, H};
+  if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
+  if (hipError_t e = mark(4)) return device_error(fn, e);
+  moe::FfnArgs dn{w.h, nullptr, w.offsets, 0, w_down, nullptr, w.row_weight, w.y, E, A, H, M};
+  if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  if (hipError_t e = mark(5)) return device_error(fn, e);
+
+  moe::CombineArgs cb{w.y, w.a2s, nullptr, w.ys, out, N, M, k};
+  if (hipError_t e = moe::launch_combine(cb, st)) return device_error(fn, e);
+  if (hipError_t e = mark(6)) return device_error(fn, e);
+  return ok();
+}
+
+}  // extern "C"

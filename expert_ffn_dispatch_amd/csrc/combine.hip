@@ -1,0 +1,56 @@
+// Combine / unpermutation: each token gathers its k expert rows through the
+// inverse mapping, weights them and sums them in slot order, then adds the
+// shared experts' output.
+//
+// Page on MoE latency (wink.run), section "router 之后还有一串动作": results are
+// restored to token order through the inverse mapping, multiplied by the
+// routing weight and summed.  Shared experts (FinDEP review, 二、核心思想) see
+// every token and add unweighted.  Sum in fp32, slots j = 0..k-1 then the
+// shared term, one bf16 rounding at the store.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ void add8(float (&acc)[8], uint4 v, float w) {
+  const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += w * __uint_as_float(q[i] << 16);
+    acc[2 * i + 1] += w * __uint_as_float(q[i] & 0xffff0000u);
+  }
+}
+
+// One block per token row; each thread owns 16-byte chunks of the row.
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs p) {
+  const int n = blockIdx.x;
+  const int chunks = p.M >> 3;
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < p.k; ++j) {
+      const int a = n * p.k + j;
+      const int pos = p.a2s[a];
+      const float w = p.weights ? p.weights[a] : 1.f;
+      add8(acc, *reinterpret_cast<const uint4*>(p.y + (size_t)pos * p.M + c * 8), w);
+    }
+    if (p.shared) add8(acc, *reinterpret_cast<const uint4*>(p.shared + (size_t)n * p.M + c * 8), 1.f);
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(p.out + (size_t)n * p.M + c * 8) = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+  if (a.N == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(a.N), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

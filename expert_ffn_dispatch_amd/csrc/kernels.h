@@ -1,0 +1,72 @@
+// Internal launchers of the MoE FFN layer's kernels (not part of the C ABI).
+// Every launcher enqueues on `st` and returns the launch status; shapes have
+// been validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  const uint16_t* x;         // [N][M]
+  const uint16_t* w_router;  // [M][E]
+  const float* bias;         // [E] or null
+  int N, M, E, k;
+  int32_t* ids;              // [N][k]
+  float* weights;            // [N][k]
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+// Dispatch + stable permutation.  Tiles of kPermTile assignments.
+constexpr int kPermTile = 256;
+struct PermuteArgs {
+  const int32_t* ids;        // [A] expert of assignment a
+  int A, E, k;
+  int32_t* counts;           // [E]
+  int32_t* offsets;          // [E+1]
+  int32_t* s2a;              // [A]
+  int32_t* a2s;              // [A]
+  int32_t* row_token;        // [A] token of sorted row p (= s2a[p] / k), or null
+  const float* weights;      // [A] routing weight per assignment, or null
+  float* row_weight;         // [A] weight in sorted order, or null
+  int32_t* tile_hist;        // [E][T] workspace
+  int32_t* tile_off;         // [E][T] workspace
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
+
+// x_sorted[p] = x[row_token[p]] or x[s2a[p] / k]
+hipError_t launch_gather(const uint16_t* x, const int32_t* s2a, int k, int A, int M, uint16_t* xs,
+                         hipStream_t st);
+
+// One phase of the grouped SwiGLU.  Rows of group e are
+// [offsets[e], offsets[e+1]) (or [0, fixed_rows) with E = 1 if fixed_rows > 0).
+struct FfnArgs {
+  // phase 1 (gate+up): A rows from `a` ([rows][K]); if a_rows is set, row p
+  // of the group reads a[a_rows[p]].  phase 2 (down): A = h.
+  const uint16_t* a;
+  const int32_t* a_rows;
+  const int32_t* offsets;    // [E+1] device, or null with fixed_rows > 0
+  int fixed_rows;
+  const uint16_t* w0;        // gate [E][H][M] | down [E][M][H]
+  const uint16_t* w1;        // up   [E][H][M] | unused
+  const float* row_scale;    // phase 2: [rows] fp32 or null
+  uint16_t* out;             // phase 1: h [rows][H]; phase 2: y [rows][M]
+  int E;                     // groups
+  int rows_total;            // upper bound on rows (N*k)
+  int K;                     // contraction: M (phase 1) | H (phase 2)
+  int ncols;                 // output columns: H (phase 1) | M (phase 2)
+};
+hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st);
+hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st);
+
+struct CombineArgs {
+  const uint16_t* y;         // [A][M] bf16
+  const int32_t* a2s;        // [A]
+  const float* weights;      // [N][k] or null
+  const uint16_t* shared;    // [N][M] or null
+  uint16_t* out;             // [N][M]
+  int N, M, k;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+}  // namespace moe

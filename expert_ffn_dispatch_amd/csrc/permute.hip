@@ -1,0 +1,162 @@
+// Dispatch and permutation: per-expert counts, exclusive-scan offsets and a
+// stable sort of the N*k assignments into expert order, plus the row gather.
+//
+// Page on MoE latency (wink.run), section "router 之后还有一串动作": top-k routing
+// turns N tokens into N*k assignments; grouping them by expert is the
+// dispatch, sorting the token rows by expert the permutation.  Order inside an
+// expert group is by assignment index a = n*k + j (stable), which makes the
+// permutation unique.
+//
+// Three launches, no atomics on anything that orders rows:
+//   hist    - one block per tile of 256 assignments: LDS histogram (integer
+//             atomics only count) -> tile_hist[e][t]
+//   scan    - one block: per expert, exclusive scan of tile_hist over tiles
+//             (wave shuffles) -> tile_off; then counts and offsets
+//   scatter - one block per tile: rank inside the tile from wave ballots
+//             (lanes with the same expert and a lower lane id) plus the
+//             counts of earlier waves, so sorted slot =
+//             offsets[e] + tile_off[e][t] + rank.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int A, int E, int T,
+                                                   int32_t* __restrict__ tile_hist) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x, tile = blockIdx.x;
+  if (tid < E) h[tid] = 0;
+  __syncthreads();
+  const int a = tile * kPermTile + tid;
+  if (a < A) atomicAdd(&h[clamp_expert(ids[a], E)], 1);
+  __syncthreads();
+  if (tid < E) tile_hist[(size_t)tid * T + tile] = h[tid];
+}
+
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ tile_hist, int E, int T,
+                                                    int32_t* __restrict__ tile_off,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets) {
+  __shared__ int cnt[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = wave; e < E; e += 16) {
+    int running = 0;
+    for (int t0 = 0; t0 < T; t0 += 64) {
+      const int t = t0 + lane;
+      const int v = (t < T) ? tile_hist[(size_t)e * T + t] : 0;
+      int inc = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(inc, off);
+        if (lane >= off) inc += o;
+      }
+      if (t < T) tile_off[(size_t)e * T + t] = running + inc - v;
+      running += __shfl(inc, 63);
+    }
+    if (lane == 0) cnt[e] = running;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int v[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      v[i] = (e < E) ? cnt[e] : 0;
+      s += v[i];
+    }
+    int inc = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    int base = inc - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      if (e < E) {
+        counts[e] = v[i];
+        offsets[e] = base;
+      }
+      base += v[i];
+    }
+    if (lane == 63) offsets[E] = inc;
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(PermuteArgs p, int T, int nbits) {
+  __shared__ int wc[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, tile = blockIdx.x;
+  for (int i = tid; i < 4 * 256; i += 256) (&wc[0][0])[i] = 0;
+  __syncthreads();
+  const int a = tile * kPermTile + tid;
+  const bool valid = a < p.A;
+  const int e = valid ? clamp_expert(p.ids[a], p.E) : 0;
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(valid && bit);
+    peers &= bit ? m : ~m;
+  }
+  const int rank = lanes_below(peers);
+  if (valid && rank == 0) wc[wave][e] = __popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wc[w][e];
+    const int pos = p.offsets[e] + p.tile_off[(size_t)e * T + tile] + before + rank;
+    p.s2a[pos] = a;
+    p.a2s[a] = pos;
+    if (p.row_token) p.row_token[pos] = a / p.k;
+    if (p.row_weight) p.row_weight[pos] = p.weights[a];
+  }
+}
+
+// Row copy: one block moves `rows` rows of M bf16 in 16-byte chunks.
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ x,
+                                                     const int32_t* __restrict__ s2a, int k, int A,
+                                                     int M, uint16_t* __restrict__ xs) {
+  const int chunks = M >> 3;
+  const int rows_per_block = (256 / chunks) > 0 ? (256 / chunks) : 1;
+  const int p0 = blockIdx.x * rows_per_block;
+  for (int i = threadIdx.x; i < rows_per_block * chunks; i += 256) {
+    const int r = i / chunks, c = i - r * chunks;
+    const int p = p0 + r;
+    if (p >= A) break;
+    const int tok = s2a[p] / k;
+    *reinterpret_cast<uint4*>(xs + (size_t)p * M + c * 8) =
+        *reinterpret_cast<const uint4*>(x + (size_t)tok * M + c * 8);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
+  const int T = ceil_div(a.A, kPermTile);
+  int nbits = 0;
+  while ((1 << nbits) < a.E) ++nbits;
+  if (T > 0) {
+    hipLaunchKernelGGL(hist_kernel, dim3(T), dim3(256), 0, st, a.ids, a.A, a.E, T, a.tile_hist);
+  }
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, a.tile_hist, a.E, T, a.tile_off,
+                     a.counts, a.offsets);
+  if (T > 0) {
+    hipLaunchKernelGGL(scatter_kernel, dim3(T), dim3(256), 0, st, a, T, nbits);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint16_t* x, const int32_t* s2a, int k, int A, int M, uint16_t* xs,
+                         hipStream_t st) {
+  if (A == 0) return hipSuccess;
+  const int chunks = M >> 3;
+  const int rpb = (256 / chunks) > 0 ? (256 / chunks) : 1;
+  hipLaunchKernelGGL(gather_kernel, dim3(ceil_div(A, rpb)), dim3(256), 0, st, x, s2a, k, A, M, xs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

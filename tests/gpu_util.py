@@ -1,0 +1,74 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, read results back,
+and the error metrics of the parity bar.
+
+Parity bar (floating point): normwise max relative error
+max|got - ref| / max|ref| <= 2e-2 and relative L2 error
+||got - ref||_2 / ||ref||_2 <= 5e-3, got upcast from bf16/fp32 to float64.
+Integer and byte outputs (ids, counts, offsets, permutation, gathered rows)
+must match bit for bit.  Routing ids are compared on tokens whose top-k
+probability margin is at least 1e-6; below that the oracle's ids are fed in.
+"""
+import sys
+
+import numpy as np
+import torch
+
+from datagen import gen
+from oracle import moe_oracle as O
+
+TOL_MAX = 2e-2
+TOL_L2 = 5e-3
+TIE_MARGIN = 1e-6
+DEV = "cuda"
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def f32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def host64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    d = np.asarray(got, np.float64) - np.asarray(ref, np.float64)
+    mref = np.abs(ref).max()
+    nref = np.linalg.norm(ref)
+    return float(np.abs(d).max() / mref), float(np.linalg.norm(d) / nref)
+
+
+def assert_close(got, ref, what: str, tol_max=TOL_MAX, tol_l2=TOL_L2):
+    mx, l2 = errors(got, ref)
+    note(f"  {what}: max_rel={mx:.3e} rel_l2={l2:.3e}")
+    assert mx <= tol_max and l2 <= tol_l2, f"{what}: max_rel={mx:.3e} (<= {tol_max}), rel_l2={l2:.3e} (<= {tol_l2})"
+
+
+def upload(d: dict) -> dict:
+    out = {}
+    for k, v in d.items():
+        if not isinstance(v, np.ndarray) or v.ndim == 0:
+            continue
+        if v.dtype == np.uint16:
+            out[k] = bf(v)
+        elif v.dtype == np.float32:
+            out[k] = f32(v)
+        elif v.dtype == np.int32:
+            out[k] = i32(v)
+    return out

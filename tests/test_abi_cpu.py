@@ -1,0 +1,142 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments on the host before anything is enqueued
+(no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_ffn_dispatch_amd as moe
+from expert_ffn_dispatch_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+FAKE = 1 << 20          # an aligned address that is never dereferenced
+MIS = FAKE + 4          # a misaligned one
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from expert_ffn_dispatch_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+    assert lib.moe_abi_version() == 1
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+def D(N=8, M=128, E=4, k=2, H=128, S=0, Hs=0):
+    return moe.dims(N, M, E, k, H, S, Hs)
+
+
+BAD_DIMS = [
+    (D(N=0), 1, "n_tokens"),
+    (D(M=100), 1, "hidden"),
+    (D(M=32), 1, "hidden"),
+    (D(E=0), 1, "n_experts"),
+    (D(E=300, k=2), 2, "n_experts"),
+    (D(k=5), 1, "top_k"),
+    (D(E=32, k=17), 1, "top_k"),
+    (D(H=96), 1, "expert_width"),
+    (D(S=1, Hs=100), 1, "n_shared*shared_width"),
+    (D(S=-1), 1, "n_shared"),
+]
+
+
+@pytest.mark.parametrize("d,code,word", BAD_DIMS, ids=[b[2] + str(i) for i, b in enumerate(BAD_DIMS)])
+def test_bad_dims(lib, d, code, word):
+    n = ctypes.c_size_t(0)
+    r = lib.moe_layer_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(n))
+    assert r == code and word in _err(lib)
+    r = lib.moe_layer(ctypes.byref(d), 0, *([FAKE] * 13), 1 << 40, None)
+    assert r == code and word in _err(lib)
+
+
+def test_route_pointer_checks(lib):
+    d = D()
+    assert lib.moe_route(ctypes.byref(d), None, FAKE, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
+    assert "x is NULL" in _err(lib)
+    assert lib.moe_route(ctypes.byref(d), MIS, FAKE, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
+    assert "aligned" in _err(lib)
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, MIS, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
+
+
+def _layer(lib, d, flags=0, ws_bytes=None, **over):
+    args = dict(x=FAKE, w_router=FAKE, router_bias=None, w_gate=FAKE, w_up=FAKE, w_down=FAKE,
+                ws_gate=None, ws_up=None, ws_down=None, topk_ids=None, topk_weights=None, out=FAKE, ws=FAKE)
+    args.update(over)
+    return lib.moe_layer(ctypes.byref(d), flags, args["x"], args["w_router"], args["router_bias"],
+                         args["w_gate"], args["w_up"], args["w_down"], args["ws_gate"], args["ws_up"],
+                         args["ws_down"], args["topk_ids"], args["topk_weights"], args["out"], args["ws"],
+                         0 if ws_bytes is None else ws_bytes, None)
+
+
+def test_layer_argument_rules(lib):
+    d = D()
+    assert _layer(lib, d, flags=8) == _lib.MOE_ERR_INVALID and "flags" in _err(lib)
+    # IDS_IN: router must be absent, ids/weights present
+    assert _layer(lib, d, flags=1) == _lib.MOE_ERR_INVALID and "w_router" in _err(lib)
+    assert _layer(lib, d, flags=1, w_router=None) == _lib.MOE_ERR_INVALID and "topk_ids" in _err(lib)
+    # router required without IDS_IN
+    assert _layer(lib, d, w_router=None) == _lib.MOE_ERR_INVALID and "w_router" in _err(lib)
+    # shared weights iff n_shared > 0
+    assert _layer(lib, d, ws_gate=FAKE) == _lib.MOE_ERR_INVALID and "n_shared" in _err(lib)
+    ds = D(S=2, Hs=64)
+    assert _layer(lib, ds) == _lib.MOE_ERR_INVALID and "ws_gate" in _err(lib)
+    # workspace
+    assert _layer(lib, d, ws=None) == _lib.MOE_ERR_WORKSPACE and "NULL" in _err(lib)
+    assert _layer(lib, d, ws_bytes=16) == _lib.MOE_ERR_WORKSPACE and "needed" in _err(lib)
+    assert _layer(lib, d, ws=FAKE + 16, ws_bytes=1 << 30) == _lib.MOE_ERR_WORKSPACE
+
+
+def test_other_entry_points_reject(lib):
+    d = D()
+    assert lib.moe_permute(ctypes.byref(d), None, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                           None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_permute(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                           None) == _lib.MOE_ERR_INVALID and "x is NULL" in _err(lib)
+    assert lib.moe_permute(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0,
+                           None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_grouped_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0,
+                               None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_grouped_ffn(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30,
+                               None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_combine(ctypes.byref(d), FAKE, FAKE, MIS, None, FAKE, None) == _lib.MOE_ERR_INVALID
+
+
+def test_workspace_sizes(lib):
+    def ws(d):
+        return moe.moe_layer_workspace_bytes(d)
+    small, big = ws(D(N=8)), ws(D(N=800))
+    assert big > small
+    d = D(N=4096, M=5120, E=160, k=6, H=1536, S=2, Hs=1536)
+    A = 4096 * 6
+    assert ws(d) >= A * 1536 * 2 + A * 5120 * 2 + 4096 * 3072 * 2 + 4096 * 5120 * 2
+    assert moe.moe_grouped_ffn_workspace_bytes(D(N=10, k=2, H=256)) >= 20 * 256 * 2
+    assert moe.moe_permute_workspace_bytes(D(N=1000, E=8, k=2)) >= 2 * 8 * 8 * 4
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libmoe_ffn.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()
