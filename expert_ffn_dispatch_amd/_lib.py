@@ -16,7 +16,8 @@ MOE_ERR_DEVICE = 4
 MOE_FLAG_IDS_IN = 1
 
 EXPORTS = (
-    "moe_abi_version", "moe_last_error", "moe_layer_workspace_bytes", "moe_permute_workspace_bytes",
+    "moe_abi_version", "moe_last_error", "moe_layer_workspace_bytes", "moe_route_workspace_bytes",
+    "moe_permute_workspace_bytes",
     "moe_grouped_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
     "moe_layer", "moe_set_stage_events",
 )
@@ -51,9 +52,9 @@ def load() -> ctypes.CDLL:
     lib.moe_last_error.restype = ctypes.c_char_p
     for name in ("moe_layer_workspace_bytes",):
         getattr(lib, name).argtypes = [DIMS, ctypes.c_uint32, ctypes.POINTER(ctypes.c_size_t)]
-    for name in ("moe_permute_workspace_bytes", "moe_grouped_ffn_workspace_bytes"):
+    for name in ("moe_route_workspace_bytes", "moe_permute_workspace_bytes", "moe_grouped_ffn_workspace_bytes"):
         getattr(lib, name).argtypes = [DIMS, ctypes.POINTER(ctypes.c_size_t)]
-    lib.moe_route.argtypes = [DIMS, P, P, P, P, P, P]
+    lib.moe_route.argtypes = [DIMS, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_permute.argtypes = [DIMS, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_grouped_ffn.argtypes = [DIMS, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_combine.argtypes = [DIMS, P, P, P, P, P, P]

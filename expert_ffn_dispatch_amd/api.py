@@ -45,6 +45,12 @@ def moe_layer_workspace_bytes(d: MoeDims, flags: int = 0) -> int:
     return n.value
 
 
+def moe_route_workspace_bytes(d: MoeDims) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().moe_route_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
 def moe_permute_workspace_bytes(d: MoeDims) -> int:
     n = ctypes.c_size_t(0)
     _lib.check(_lib.load().moe_permute_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
@@ -61,15 +67,19 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def moe_route(d: MoeDims, x, w_router, router_bias=None, topk_ids=None, topk_weights=None, stream=None):
+def moe_route(d: MoeDims, x, w_router, router_bias=None, topk_ids=None, topk_weights=None, ws=None,
+              stream=None):
     dev = x.device
     if topk_ids is None:
         topk_ids = torch.empty((d.n_tokens, d.top_k), dtype=torch.int32, device=dev)
     if topk_weights is None:
         topk_weights = torch.empty((d.n_tokens, d.top_k), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(moe_route_workspace_bytes(d), dev)
     _lib.check(_lib.load().moe_route(ctypes.byref(d), _ptr(x, _BF16_LIKE), _ptr(w_router, _BF16_LIKE),
                                      _ptr(router_bias, (torch.float32,)), _ptr(topk_ids, (torch.int32,)),
-                                     _ptr(topk_weights, (torch.float32,)), _stream(stream)))
+                                     _ptr(topk_weights, (torch.float32,)), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
     return topk_ids, topk_weights
 
 

@@ -107,6 +107,7 @@ PermuteWs carve_permute(Carver& c, int A, int E) {
 }
 
 struct LayerWs {
+  void* route;
   int32_t* ids;
   float* wts;
   int32_t* counts;
@@ -125,6 +126,7 @@ LayerWs carve_layer(Carver& c, const moe_dims& d) {
   const size_t N = d.n_tokens, A = (size_t)d.n_tokens * d.top_k, E = d.n_experts;
   const size_t SH = (size_t)d.n_shared * (d.n_shared > 0 ? d.shared_width : 0);
   LayerWs w;
+  w.route = c.take<char>(moe::route_workspace_bytes(d.n_tokens, d.hidden, d.n_experts));
   w.ids = c.take<int32_t>(A);
   w.wts = c.take<float>(A);
   w.counts = c.take<int32_t>(E);
@@ -198,6 +200,14 @@ int moe_layer_workspace_bytes(const moe_dims* dims, uint32_t flags, size_t* byte
   return ok();
 }
 
+int moe_route_workspace_bytes(const moe_dims* dims, size_t* bytes) {
+  const char* fn = "moe_route_workspace_bytes";
+  if (int r = check_dims(fn, dims, false)) return r;
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID, "%s: bytes is NULL", fn);
+  *bytes = moe::route_workspace_bytes(dims->n_tokens, dims->hidden, dims->n_experts);
+  return ok();
+}
+
 int moe_permute_workspace_bytes(const moe_dims* dims, size_t* bytes) {
   const char* fn = "moe_permute_workspace_bytes";
   if (int r = check_dims(fn, dims, false)) return r;
@@ -219,7 +229,8 @@ int moe_grouped_ffn_workspace_bytes(const moe_dims* dims, size_t* bytes) {
 }
 
 int moe_route(const moe_dims* dims, const moe_bf16* x, const moe_bf16* w_router,
-              const float* router_bias, int32_t* topk_ids, float* topk_weights, moe_stream stream) {
+              const float* router_bias, int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
+              moe_stream stream) {
   const char* fn = "moe_route";
   if (int r = check_dims(fn, dims, false)) return r;
   REQ_PTR(x);
@@ -227,9 +238,11 @@ int moe_route(const moe_dims* dims, const moe_bf16* x, const moe_bf16* w_router,
   OPT_PTR(router_bias);
   REQ_PTR(topk_ids);
   REQ_PTR(topk_weights);
+  if (int r = check_ws(fn, ws, ws_bytes, moe::route_workspace_bytes(dims->n_tokens, dims->hidden, dims->n_experts)))
+    return r;
   moe::RouteArgs a{x, w_router, router_bias, dims->n_tokens, dims->hidden, dims->n_experts, dims->top_k,
                    topk_ids, topk_weights};
-  if (hipError_t e = moe::launch_route(a, static_cast<hipStream_t>(stream))) return device_error(fn, e);
+  if (hipError_t e = moe::launch_route(a, ws, static_cast<hipStream_t>(stream))) return device_error(fn, e);
   return ok();
 }
 
@@ -357,7 +370,7 @@ int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe
 
   if (!ids_in) {
     moe::RouteArgs r{x, w_router, router_bias, N, M, E, k, ids, wts};
-    if (hipError_t e = moe::launch_route(r, st)) return device_error(fn, e);
+    if (hipError_t e = moe::launch_route(r, w.route, st)) return device_error(fn, e);
   }
   if (hipError_t e = mark(1)) return device_error(fn, e);
   moe::PermuteArgs p{ids, A, E, k, w.counts, w.offsets, w.s2a, w.a2s, w.row_token, wts, w.row_weight,

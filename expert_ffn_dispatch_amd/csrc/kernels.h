@@ -15,7 +15,8 @@ struct RouteArgs {
   int32_t* ids;              // [N][k]
   float* weights;            // [N][k]
 };
-hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+size_t route_workspace_bytes(int N, int M, int E);
+hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st);
 
 // Dispatch + stable permutation.  Tiles of kPermTile assignments.
 constexpr int kPermTile = 256;

@@ -8,6 +8,16 @@
 // monotone), so selection runs on the logits and only the k winners are
 // exponentiated: w_j = exp(l_j - l_max) / sum_sel exp(l_i - l_max), which is
 // p_j / sum_sel p.  Ties go to the lower expert id; slot 0 holds the largest.
+//
+// Three launches:
+//   transpose - W_r [M][E] -> W_rT [EP][M] (E padded to 16), so that both MFMA
+//               operands read 16 contiguous bytes of the contraction per lane
+//   logits    - one wave per (16 tokens, k slice): partial scores for all
+//               experts; the contraction is split into KS slices so that even
+//               a decode batch spreads over hundreds of waves
+//   topk      - one wave per token: sums the KS partials in slice order
+//               (deterministic), adds the bias, wave-wide arg-max k times
+//               (ties to the lower id), renormalises.
 #include "common.h"
 #include "kernels.h"
 
@@ -15,165 +25,184 @@ namespace moe {
 
 namespace {
 
-constexpr int kTok = 64;              // tokens per block: 4 waves x 16 rows
-constexpr int kBK = 64;               // contraction slab
-constexpr int kLd = kBK + 8;          // LDS row pitch (bf16) with 16 B pad
-
-// ncb = number of 16-expert column blocks held by each wave (E padded).
-template <int NCB, bool VEC>
-__global__ __launch_bounds__(256) void route_kernel(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ wr,
-                                                    const float* __restrict__ bias, int N, int M,
-                                                    int E, int k, int32_t* __restrict__ ids,
-                                                    float* __restrict__ wts) {
-  constexpr int EP = NCB * 16;
-  extern __shared__ __align__(16) char smem[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);   // [kTok][kLd]
-  uint16_t* wt = xs + kTok * kLd;                      // [EP][kLd]  (router transposed)
-  float* lg = reinterpret_cast<float*>(smem);          // [kTok][EP] after the K loop
-
+__global__ __launch_bounds__(256) void router_transpose_kernel(const uint16_t* __restrict__ wr, int M, int E,
+                                                               int EP, uint16_t* __restrict__ wt) {
+  __shared__ uint16_t t[64][66];
+  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int tok0 = blockIdx.x * kTok;
+  for (int i = tid; i < 64 * 64; i += 256) {
+    const int kk = i >> 6, ee = i & 63;
+    const int e = e0 + ee;
+    t[kk][ee] = (e < E) ? wr[(size_t)(k0 + kk) * E + e] : 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < 64 * 64; i += 256) {
+    const int ee = i >> 6, kk = i & 63;
+    const int e = e0 + ee;
+    if (e < EP) wt[(size_t)e * M + k0 + kk] = t[kk][ee];
+  }
+}
 
-  // padded expert rows stay zero
-  for (int i = tid; i < (EP - E) * kLd; i += 256) wt[E * kLd + i] = 0;
+// part[ks][n][e] = sum over the slice's k of x[n,k] * W_r[k,e]
+template <int NCB>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wt, int N, int M,
+                                                            int steps_per_slice, float* __restrict__ part) {
+  constexpr int EP = NCB * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tg = blockIdx.x * 4 + wave;
+  const int tok0 = tg * 16;
+  if (tok0 >= N) return;
+  const int ks = blockIdx.y;
+  const int s0 = ks * steps_per_slice;
+  const int s1 = min(M / 32, s0 + steps_per_slice);
+  const int r = lane & 15, g = lane >> 4;
+  const int tok = min(tok0 + r, N - 1);
+  const uint16_t* xa = x + (size_t)tok * M + g * 8;
+  const uint16_t* wb = wt + (size_t)r * M + g * 8;
 
   f32x4_t acc[NCB];
 #pragma unroll
   for (int c = 0; c < NCB; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < M; k0 += kBK) {
-    // x slab: 64 rows x 8 chunks of 16 B
+  uint4 a = *reinterpret_cast<const uint4*>(xa + s0 * 32);
+  uint4 b[NCB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 3, ch = c & 7;
-      const int n = tok0 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < N) v = *reinterpret_cast<const uint4*>(x + (size_t)n * M + k0 + ch * 8);
-      *reinterpret_cast<uint4*>(xs + r * kLd + ch * 8) = v;
-    }
-    // router slab [kBK][E] -> wt[e][kk]
-    if (VEC) {
-      const int e8n = E >> 3;
-      for (int u = tid; u < kBK * e8n; u += 256) {
-        const int kk = u / e8n, e8 = u - kk * e8n;
-        const uint4 v = *reinterpret_cast<const uint4*>(wr + (size_t)(k0 + kk) * E + e8 * 8);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  for (int c = 0; c < NCB; ++c) b[c] = *reinterpret_cast<const uint4*>(wb + (size_t)c * 16 * M + s0 * 32);
+  for (int s = s0; s < s1; ++s) {
+    const int sn = (s + 1 < s1) ? s + 1 : s;
+    const uint4 an = *reinterpret_cast<const uint4*>(xa + sn * 32);
+    uint4 bn[NCB];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          wt[(e8 * 8 + 2 * q) * kLd + kk] = static_cast<uint16_t>(w4[q] & 0xffffu);
-          wt[(e8 * 8 + 2 * q + 1) * kLd + kk] = static_cast<uint16_t>(w4[q] >> 16);
-        }
-      }
-    } else {
-      for (int u = tid; u < kBK * E; u += 256) {
-        const int kk = u / E, e = u - kk * E;
-        wt[e * kLd + kk] = wr[(size_t)(k0 + kk) * E + e];
-      }
-    }
-    __syncthreads();
+    for (int c = 0; c < NCB; ++c) bn[c] = *reinterpret_cast<const uint4*>(wb + (size_t)c * 16 * M + sn * 32);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kc = ks * 32 + (lane >> 4) * 8;
-      const uint4 a = *reinterpret_cast<const uint4*>(xs + (wave * 16 + (lane & 15)) * kLd + kc);
+    for (int c = 0; c < NCB; ++c) acc[c] = mfma16(a, b[c], acc[c]);
+    a = an;
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        const uint4 b = *reinterpret_cast<const uint4*>(wt + (c * 16 + (lane & 15)) * kLd + kc);
-        acc[c] = mfma16(a, b, acc[c]);
-      }
-    }
-    __syncthreads();
+    for (int c = 0; c < NCB; ++c) b[c] = bn[c];
   }
-
-  // logits (+ bias) to LDS: lane holds rows 4*(lane>>4)+r, expert c*16+(lane&15)
+  float* out = part + (size_t)ks * N * EP;
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) {
-    const int e = c * 16 + (lane & 15);
-    const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
+  for (int q = 0; q < 4; ++q) {
+    const int n = tok0 + g * 4 + q;
+    if (n >= N) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lg[(wave * 16 + (lane >> 4) * 4 + r) * EP + e] = acc[c][r] + b;
+    for (int c = 0; c < NCB; ++c) out[(size_t)n * EP + c * 16 + r] = acc[c][q];
   }
-  __syncthreads();
+}
 
-  constexpr int PER = (EP + 63) / 64;   // experts per lane
-  for (int t = 0; t < 16; ++t) {
-    const int row = wave * 16 + t;
-    const int n = tok0 + row;
-    if (n >= N) break;
-    float v[PER];
-    bool taken[PER];
+template <int PER>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part, const float* __restrict__ bias,
+                                                          int N, int E, int EP, int KS, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  float v[PER];
+  bool taken[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    float s = 0.f;
+    if (e < E) {
+      for (int ks = 0; ks < KS; ++ks) s += part[((size_t)ks * N + n) * EP + e];
+      if (bias) s += bias[e];
+    }
+    v[i] = s;
+    taken[i] = !(e < E);
+  }
+  int my_e = 0;
+  float my_v = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.f;
+    int be = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lane + 64 * i;
-      v[i] = (e < E) ? lg[row * EP + e] : 0.f;
-      taken[i] = !(e < E);
+      if (!taken[i] && (be == 0x7fffffff || v[i] > bv)) { bv = v[i]; be = e; }
     }
-    int my_e = 0;
-    float my_v = 0.f;
-    for (int j = 0; j < k; ++j) {
-      float bv = 0.f;
-      int be = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = lane + 64 * i;
-        if (!taken[i] && (be == 0x7fffffff || v[i] > bv)) { bv = v[i]; be = e; }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        const bool better = (oe != 0x7fffffff) &&
-                            (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-        if (better) { bv = ov; be = oe; }
-      }
-      if (lane == j) { my_e = be; my_v = bv; }
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (lane + 64 * i == be) taken[i] = true;
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      const bool better = (oe != 0x7fffffff) && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+      if (better) { bv = ov; be = oe; }
     }
-    const float vmax = __shfl(my_v, 0);
-    float ex = (lane < k) ? __expf(my_v - vmax) : 0.f;
-    float s = ex;
+    if (lane == j) { my_e = be; my_v = bv; }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane < k) {
-      ids[(size_t)n * k + lane] = my_e;
-      wts[(size_t)n * k + lane] = ex / s;
-    }
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i == be) taken[i] = true;
+  }
+  const float vmax = __shfl(my_v, 0);
+  const float ex = (lane < k) ? __expf(my_v - vmax) : 0.f;
+  float s = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane < k) {
+    ids[(size_t)n * k + lane] = my_e;
+    wts[(size_t)n * k + lane] = ex / s;
   }
 }
 
-template <int NCB, bool VEC>
-hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
-  constexpr int EP = NCB * 16;
-  const size_t lds_k = (size_t)(kTok + EP) * kLd * 2;
-  const size_t lds_l = (size_t)kTok * EP * 4;
-  const size_t lds = lds_k > lds_l ? lds_k : lds_l;
-  const int grid = ceil_div(a.N, kTok);
-  hipLaunchKernelGGL((route_kernel<NCB, VEC>), dim3(grid), dim3(256), lds, st, a.x, a.w_router,
-                     a.bias, a.N, a.M, a.E, a.k, a.ids, a.weights);
-  return hipGetLastError();
+struct RoutePlan {
+  int NCB, EP, KS, steps;
+};
+
+RoutePlan plan(int N, int M, int E) {
+  RoutePlan p;
+  const int ncb = ceil_div(E, 16);
+  p.NCB = ncb <= 1 ? 1 : ncb <= 2 ? 2 : ncb <= 4 ? 4 : ncb <= 8 ? 8 : ncb <= 10 ? 10 : ncb <= 12 ? 12 : 16;
+  p.EP = p.NCB * 16;
+  const int tg = ceil_div(N, 16);
+  const int total_steps = M / 32;
+  int ks = ceil_div(2048, tg);
+  const int max_ks = ceil_div(total_steps, 4);      // slices of at least 128 k
+  if (ks > max_ks) ks = max_ks;
+  if (ks < 1) ks = 1;
+  p.steps = ceil_div(total_steps, ks);
+  p.KS = ceil_div(total_steps, p.steps);
+  return p;
 }
 
-template <bool VEC>
-hipError_t launch_route_v(const RouteArgs& a, hipStream_t st) {
-  const int ncb = ceil_div(a.E, 16);
-  if (ncb <= 1) return launch_route_t<1, VEC>(a, st);
-  if (ncb <= 2) return launch_route_t<2, VEC>(a, st);
-  if (ncb <= 4) return launch_route_t<4, VEC>(a, st);
-  if (ncb <= 8) return launch_route_t<8, VEC>(a, st);
-  if (ncb <= 12) return launch_route_t<12, VEC>(a, st);
-  return launch_route_t<16, VEC>(a, st);
+template <int NCB>
+void launch_logits(const RouteArgs& a, const RoutePlan& pl, const uint16_t* wt, float* part, hipStream_t st) {
+  hipLaunchKernelGGL((router_logits_kernel<NCB>), dim3(ceil_div(a.N, 64), pl.KS), dim3(256), 0, st, a.x, wt,
+                     a.N, a.M, pl.steps, part);
 }
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+size_t route_workspace_bytes(int N, int M, int E) {
+  const RoutePlan pl = plan(N, M, E);
+  const size_t wt = ((size_t)pl.EP * M * 2 + 255) & ~size_t(255);
+  const size_t part = ((size_t)pl.KS * N * pl.EP * 4 + 255) & ~size_t(255);
+  return wt + part;
+}
+
+hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
-  return (a.E % 8 == 0) ? launch_route_v<true>(a, st) : launch_route_v<false>(a, st);
+  const RoutePlan pl = plan(a.N, a.M, a.E);
+  uint16_t* wt = static_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + (((size_t)pl.EP * a.M * 2 + 255) & ~size_t(255)));
+  hipLaunchKernelGGL(router_transpose_kernel, dim3(a.M / 64, ceil_div(pl.EP, 64)), dim3(256), 0, st, a.w_router,
+                     a.M, a.E, pl.EP, wt);
+  switch (pl.NCB) {
+    case 1: launch_logits<1>(a, pl, wt, part, st); break;
+    case 2: launch_logits<2>(a, pl, wt, part, st); break;
+    case 4: launch_logits<4>(a, pl, wt, part, st); break;
+    case 8: launch_logits<8>(a, pl, wt, part, st); break;
+    case 10: launch_logits<10>(a, pl, wt, part, st); break;
+    case 12: launch_logits<12>(a, pl, wt, part, st); break;
+    default: launch_logits<16>(a, pl, wt, part, st); break;
+  }
+  const int per = ceil_div(pl.EP, 64);
+  const dim3 g(ceil_div(a.N, 4));
+  if (per <= 1)
+    hipLaunchKernelGGL(router_topk_kernel<1>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
+  else if (per <= 2)
+    hipLaunchKernelGGL(router_topk_kernel<2>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<4>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -95,8 +95,9 @@ const char* moe_last_error(void);
 /* Workspace moe_layer needs for `dims` and `flags`, in bytes (host). */
 int moe_layer_workspace_bytes(const moe_dims* dims, uint32_t flags, size_t* bytes);
 
-/* Workspace moe_permute / moe_grouped_ffn need, in bytes (host).  For
- * moe_grouped_ffn the dims are those of the call (E groups, N*k rows). */
+/* Workspace moe_route / moe_permute / moe_grouped_ffn need, in bytes (host).
+ * For moe_grouped_ffn the dims are those of the call (E groups, N*k rows). */
+int moe_route_workspace_bytes(const moe_dims* dims, size_t* bytes);
 int moe_permute_workspace_bytes(const moe_dims* dims, size_t* bytes);
 int moe_grouped_ffn_workspace_bytes(const moe_dims* dims, size_t* bytes);
 
@@ -113,10 +114,11 @@ int moe_grouped_ffn_workspace_bytes(const moe_dims* dims, size_t* bytes);
  *
  * x [N][M] bf16; w_router [M][E] bf16; router_bias [E] fp32 or NULL;
  * topk_ids [N][k] int32 (out); topk_weights [N][k] fp32 (out).
+ * ws: moe_route_workspace_bytes (the transposed router and partial scores).
  */
 int moe_route(const moe_dims* dims, const moe_bf16* x, const moe_bf16* w_router,
               const float* router_bias, int32_t* topk_ids, float* topk_weights,
-              moe_stream stream);
+              void* ws, size_t ws_bytes, moe_stream stream);
 
 /*
  * moe_permute - dispatch (per-expert counts and offsets) and the permutation

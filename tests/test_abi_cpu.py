@@ -73,11 +73,13 @@ def test_bad_dims(lib, d, code, word):
 
 def test_route_pointer_checks(lib):
     d = D()
-    assert lib.moe_route(ctypes.byref(d), None, FAKE, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_route(ctypes.byref(d), None, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == _lib.MOE_ERR_INVALID
     assert "x is NULL" in _err(lib)
-    assert lib.moe_route(ctypes.byref(d), MIS, FAKE, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_route(ctypes.byref(d), MIS, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == _lib.MOE_ERR_INVALID
     assert "aligned" in _err(lib)
-    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, MIS, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, MIS, FAKE, FAKE, FAKE, 1 << 30, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
+    assert moe.moe_route_workspace_bytes(D(N=156, M=6144, E=8)) >= 16 * 6144 * 2
 
 
 def _layer(lib, d, flags=0, ws_bytes=None, **over):
