@@ -12,11 +12,12 @@
 // Phase 2 (down): y = (h W_d^T) * row_scale.
 //
 // Two kernels, chosen on the host from the mean rows per expert (N*k/E):
-//  * stream (decode-sized groups, <= 64 mean rows): every wave owns 16 output
-//    columns and streams its weight rows from HBM straight into MFMA
-//    registers, one 128-wide k chunk ahead; the group's token rows (at most
-//    64 per pass) are staged in LDS and shared by the four waves.  Weights
-//    are read once per pass; the kernel is bound by HBM bandwidth.
+//  * stream (decode-sized groups, <= 56 mean rows): every wave owns 16 output
+//    columns and streams its weight rows from HBM (row-contiguous loads two
+//    chunks ahead, staged through a wave-private LDS slot); the group's token
+//    rows (at most 64 per pass) are staged in LDS and shared by the four
+//    waves.  Weights are read once per pass; the kernel is bound by HBM
+//    bandwidth.
 //  * tile (large groups): 256-row x 256-column tiles, both operands staged
 //    through LDS (register double buffering, 16-byte chunks XOR-swizzled by
 //    row so MFMA fragment reads are free of bank conflicts), four waves of
@@ -32,16 +33,30 @@ namespace moe {
 namespace {
 
 // =========================== streaming kernel ==============================
+//
+// Weights are read row-contiguously: one load instruction covers 4 weight
+// rows x 256 contiguous bytes (16 lanes per row), which keeps the DRAM and L2
+// request stream dense (an MFMA-fragment-shaped load touches 16 rows x 64 B
+// and streams markedly slower).  Each wave owns 16 output columns; its
+// weight chunks are prefetched LA = 2 chunks ahead into registers, then
+// staged through a wave-private LDS slot (16-byte chunks XOR-swizzled by row)
+// from which the MFMA fragments are read.  Only the token rows (A) are shared
+// by the block's four waves: double-buffered in LDS, one barrier per chunk.
 
-constexpr int kSK = 128;   // k per chunk
+constexpr int kSK = 128;   // k per chunk: 256 B of every weight row
 constexpr int kSCols = 16; // output columns per wave
-
-template <int FM, bool GATEUP>
-__global__ __launch_bounds__(256, (FM <= 3 ? 3 : 2)) void ffn_stream_kernel(FfnArgs p) {
+// LA: weight chunks in flight per wave (registers)
+template <int FM, bool GATEUP, int LA>
+__global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
   constexpr int RB = FM * 16;
-  constexpr int NMAT = GATEUP ? 2 : 1;
-  constexpr int BNC = 4 * kSCols;
+  // every wave streams two groups of 16 weight rows: gate and up rows of the
+  // same 16 h columns, or (down) 32 consecutive rows of W_down = 32 columns
+  constexpr int NMAT = 2;
+  constexpr int WCOLS = GATEUP ? kSCols : 2 * kSCols;   // output columns per wave
+  constexpr int BNC = 4 * WCOLS;
+  constexpr int AL = RB * 16 / 256;          // A uint4 per thread per chunk
   __shared__ __align__(16) uint16_t sa[2][RB * kSK];
+  __shared__ __align__(16) uint16_t sb[4][NMAT][kSCols * kSK];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tp[kMaxGroups + 1];
 
@@ -49,246 +64,311 @@ __global__ __launch_bounds__(256, (FM <= 3 ? 3 : 2)) void ffn_stream_kernel(FfnA
   const int K = p.K, ncols = p.ncols;
   const int NT = ncols / BNC;
   const int NC = K / kSK;                     // the host sends only K % 128 == 0 here
-  const int total = build_tile_list<0>(p, NT, s_off, s_tp);
+  // one tile = (group, pass of RB rows, 64 output columns); one tile per block
+  const int total = build_tile_list<RB>(p, NT, s_off, s_tp);
+  // Tiles follow the block index.  (Dealing one expert's tiles to a single
+  // XCD keeps its token rows in one L2 but measured ~20% slower: eight
+  // XCDs each streaming one contiguous weight region.)
+  const int tile = blockIdx.x;
+  if (tile >= total) return;
+  const int e = find_group(s_tp, p.E, tile);
+  const int cnt = s_off[e + 1] - s_off[e];
+  const int RT = ceil_div(cnt, RB);
+  const int local = tile - s_tp[e];
+  const int ct = local / RT, rt = local - ct * RT;
+  const int row0 = s_off[e] + rt * RB;
+  const int nrows = min(RB, cnt - rt * RB);
+  const int col0 = ct * BNC + wave * WCOLS;
 
-  // one tile per block; blocks past the end of the list exit
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int e = find_group(s_tp, p.E, tile);
-    const int ct = tile - s_tp[e];
-    const int base = s_off[e];
-    const int cnt = s_off[e + 1] - base;
-    const int col0 = ct * BNC + wave * kSCols;
-    const uint16_t* wb[NMAT];
-    wb[0] = p.w0 + ((size_t)e * ncols + col0 + (lane & 15)) * K + (lane >> 4) * 8;
-    if (GATEUP) wb[NMAT - 1] = p.w1 + ((size_t)e * ncols + col0 + (lane & 15)) * K + (lane >> 4) * 8;
+  // weight load mapping: instruction i covers rows 4i + (lane >> 4), 16-byte chunk lane & 15
+  const int brow = lane >> 4, bch = lane & 15;
+  const size_t wrow = ((size_t)e * ncols + col0 + brow) * K + bch * 8;
+  const uint16_t* wb0 = p.w0 + wrow;
+  const uint16_t* wb1 = GATEUP ? p.w1 + wrow : p.w0 + wrow + (size_t)kSCols * K;
+  int bdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + brow;
+    bdst[i] = r * kSK + ((bch ^ r) << 3);
+  }
+  const int fr = lane & 15;                   // MFMA fragment row / column
 
-    for (int r0 = 0; r0 < cnt; r0 += RB) {
-      const int nrows = min(RB, cnt - r0);
-      uint32_t aoff[FM];
-      int adst[FM];
+  uint32_t aoff[AL];
+  int adst[AL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int r = (tid >> 4) + 16 * i, ch = tid & 15;
+    const int rr = (r < nrows) ? r : 0;
+    const int grow = p.a_rows ? p.a_rows[row0 + rr] : (row0 + rr);
+    aoff[i] = (uint32_t)grow * (uint32_t)K + ch * 8;
+    adst[i] = r * kSK + ((ch ^ (r & 15)) << 3);
+  }
+  f32x4_t acc[NMAT][FM];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[m][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: chunk 0 straight into LDS, chunks 1..LA into registers
+  uint4 bq[LA][NMAT][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    *reinterpret_cast<uint4*>(&sb[wave][0][bdst[i]]) = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K);
+    *reinterpret_cast<uint4*>(&sb[wave][1][bdst[i]]) = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K);
+  }
+#pragma unroll
+  for (int l = 0; l < LA; ++l) {
+    const int ko = (1 + l < NC ? 1 + l : NC - 1) * kSK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bq[l][0][i] = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K + ko);
+      bq[l][1][i] = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K + ko);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < AL; ++i)
+    *reinterpret_cast<uint4*>(&sa[0][adst[i]]) = *reinterpret_cast<const uint4*>(p.a + aoff[i]);
+  __syncthreads();
+
+  for (int c = 0; c < NC; ++c) {
+    // the last chunk re-reads itself so loads and stores stay unconditional
+    const int ka = (c + 1 < NC ? c + 1 : c) * kSK;
+    uint4 ra[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ka);
+    const uint16_t* L = sa[c & 1];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int ch = s * 4 + (lane >> 4);
+      uint4 bf[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+        bf[m] = *reinterpret_cast<const uint4*>(&sb[wave][m][fr * kSK + ((ch ^ fr) << 3)]);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int r = (tid >> 4) + 16 * i, ch = tid & 15;
-        const int rr = (r < nrows) ? r : 0;
-        const int grow = p.a_rows ? p.a_rows[base + r0 + rr] : (base + r0 + rr);
-        aoff[i] = (uint32_t)grow * (uint32_t)K + ch * 8;
-        adst[i] = r * kSK + ((ch ^ (r & 15)) << 3);
+        const int r = i * 16 + fr;
+        const uint4 af = *reinterpret_cast<const uint4*>(&L[r * kSK + ((ch ^ (r & 15)) << 3)]);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) acc[m][i] = mfma16(af, bf[m], acc[m][i]);
       }
-      f32x4_t acc[NMAT][FM];
+    }
+    // chunk c+1 (oldest registers) into this wave's LDS slot, after this
+    // wave's reads of chunk c; rotate; fetch chunk c+1+LA
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sb[wave][m][bdst[i]]) = bq[0][m][i];
+#pragma unroll
+    for (int l = 0; l + 1 < LA; ++l)
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[m][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-      // B fragments for chunk c live in bc; chunk c+1 is in flight in bn
-      // while chunk c is multiplied.
-      uint4 bc[NMAT][4], bn[NMAT][4];
+        for (int i = 0; i < 4; ++i) bq[l][m][i] = bq[l + 1][m][i];
+    {
+      const int cn = c + 1 + LA;
+      const int ko = (cn < NC ? cn : NC - 1) * kSK;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        *reinterpret_cast<uint4*>(&sa[0][adst[i]]) = *reinterpret_cast<const uint4*>(p.a + aoff[i]);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bc[m][s] = *reinterpret_cast<const uint4*>(wb[m] + 32 * s);
-      __syncthreads();
-
-      for (int c = 0; c < NC; ++c) {
-        // the last chunk re-reads itself so that loads and stores stay
-        // unconditional (keeps the staging arrays in registers)
-        const int ko = (c + 1 < NC ? c + 1 : c) * kSK;
-        uint4 ra[FM];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) bn[m][s] = *reinterpret_cast<const uint4*>(wb[m] + ko + 32 * s);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) ra[i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ko);
-        const uint16_t* L = sa[c & 1];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int ch = s * 4 + (lane >> 4);
-#pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int r = i * 16 + (lane & 15);
-            const uint4 af = *reinterpret_cast<const uint4*>(&L[r * kSK + ((ch ^ (r & 15)) << 3)]);
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) acc[m][i] = mfma16(af, bc[m][s], acc[m][i]);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) *reinterpret_cast<uint4*>(&sa[(c + 1) & 1][adst[i]]) = ra[i];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) bc[m][s] = bn[m][s];
-        __syncthreads();
+      for (int i = 0; i < 4; ++i) {
+        bq[LA - 1][0][i] = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K + ko);
+        bq[LA - 1][1][i] = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K + ko);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < AL; ++i) *reinterpret_cast<uint4*>(&sa[(c + 1) & 1][adst[i]]) = ra[i];
+    __syncthreads();
+  }
 
-      const int col = col0 + (lane & 15);
+  const int col = col0 + fr;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = i * 16 + (lane >> 4) * 4 + q;
-          if (r >= nrows) continue;
-          const int orow = base + r0 + r;
-          float v;
-          if (GATEUP) {
-            const float g = acc[0][i][q], u = acc[NMAT - 1][i][q];
-            v = g / (1.f + __expf(-g)) * u;
-          } else {
-            v = acc[0][i][q] * (p.row_scale ? p.row_scale[orow] : 1.f);
-          }
-          p.out[(size_t)orow * ncols + col] = f32_to_bf16(v);
-        }
+    for (int q = 0; q < 4; ++q) {
+      const int r = i * 16 + (lane >> 4) * 4 + q;
+      if (r >= nrows) continue;
+      const int orow = row0 + r;
+      if (GATEUP) {
+        const float g = acc[0][i][q], u = acc[1][i][q];
+        p.out[(size_t)orow * ncols + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+      } else {
+        const float sc = p.row_scale ? p.row_scale[orow] : 1.f;
+        p.out[(size_t)orow * ncols + col] = f32_to_bf16(acc[0][i][q] * sc);
+        p.out[(size_t)orow * ncols + col + kSCols] = f32_to_bf16(acc[1][i][q] * sc);
       }
     }
   }
 }
 
 // ============================== tiled kernel ===============================
+//
+// 256 rows x 256 weight rows per tile (gate+up: 128 gate and the same 128 up
+// rows, i.e. 128 h columns; down: 256 output columns), eight waves in a 2 x 4
+// grid, each 128 rows x 64 weight rows, bf16 MFMA 32x32x16 (fp32 accumulate;
+// on gfx950 this shape sustains close to peak from few waves).  The k loop
+// walks 32-wide stages: every thread loads its four 16-byte chunks of stage
+// kt+3 into registers while stage kt is multiplied from LDS, and writes stage
+// kt+1 into the free LDS buffer (two LDS buffers, one barrier per stage).
+// Each LDS row is 64 B (4 chunks of 16 B); chunk c of row r lives at
+// c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which makes the 32-row fragment
+// reads conflict-free for both 32- and 64-bank LDS.  (Loading straight into
+// LDS would save the staging registers, but the compiler then waits for every
+// such load in flight before any LDS read, which serialises the ring.)
 
-constexpr int kBK = 64;   // contraction slab: 8 chunks of 16 B per row
+constexpr int kTBK = 32;      // k per stage
+constexpr int kTM = 256;      // rows per tile
+constexpr int kTN = 256;      // weight rows per tile
+constexpr int kTStage = (kTM + kTN) * kTBK;   // bf16 elements per stage (32 KB)
 
-__device__ __forceinline__ int swz8(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
-__global__ __launch_bounds__(256) void ffn_tile_kernel(FfnArgs p) {
-  constexpr int NB = GATEUP ? 2 * BN : BN;   // weight rows per tile
-  constexpr int TM = BM / WM, TN = BN / WN;  // wave tile (output)
-  constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int NACC = GATEUP ? 2 : 1;
-  constexpr int A_LD = BM * 8 / 256;
-  constexpr int B_LD = NB * 8 / 256;
-  static_assert(BM % 32 == 0 && NB % 32 == 0 && TM % 16 == 0 && TN % 16 == 0, "tile shape");
-  static_assert(WM * WN == 4, "four waves");
+__device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
 
-  extern __shared__ __align__(16) uint16_t lds[];   // [2][(BM + NB) * kBK]
+__device__ __forceinline__ int tsw(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+template <bool GATEUP>
+__global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
+  constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
+  __shared__ __align__(16) uint16_t sbuf[2][kTStage];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tp[kMaxGroups + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave >> 2, wn = wave & 3;       // 2 x 4 waves
   const int K = p.K, ncols = p.ncols;
-  const int NT = ncols / BN;
-  const int total = build_tile_list<BM>(p, NT, s_off, s_tp);
-  const int G = gridDim.x;
-  const int per_xcd = G >> 3;              // G is a multiple of 8
-  const int slot = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  constexpr int STAGE = (BM + NB) * kBK;
+  const int NT = ceil_div(ncols, HC);            // the last column tile may be partial
+  const int KT = K / kTBK;
+  const int total = build_tile_list<kTM>(p, NT, s_off, s_tp);
+  const int G = gridDim.x;                       // a multiple of 8
+  const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int fr = lane & 31, fg = lane >> 5;
 
-  for (int round = 0;; ++round) {
+  // LDS offsets of this lane's fragments for k step s in {0, 1}: row -> the
+  // swizzled slot of chunk 2s + fg
+  int aro[4][2], bro[2][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + 32 * i + fr;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) aro[i][s] = ra * kTBK + (((2 * s + fg) ^ tsw(ra)) << 3);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    // gate+up: block 0 = gate rows of this wave's 32 h columns, block 1 = the up rows
+    const int cb = GATEUP ? (j == 0 ? wn * 32 : HC + wn * 32) : wn * 64 + 32 * j;
+    const int rb = kTM + cb + fr;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) bro[j][s] = rb * kTBK + (((2 * s + fg) ^ tsw(rb)) << 3);
+  }
+  // this thread's four 16-byte chunks per stage: tile row tid/4 + 128*i
+  // (i = 0, 1: token rows; i = 2, 3: weight rows), chunk tid & 3
+  const int lch = tid & 3;
+  int ldst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 2) + 128 * i;
+    ldst[i] = r * kTBK + ((lch ^ tsw(r)) << 3);
+  }
+
+  for (int round = 0; round * G < total; ++round) {
     const int tile = round * G + slot;
-    if (round * G >= total) break;
     if (tile >= total) continue;
     const int e = find_group(s_tp, p.E, tile);
     const int cnt = s_off[e + 1] - s_off[e];
-    const int RT = ceil_div(cnt, BM);
+    const int RT = ceil_div(cnt, kTM);
     const int local = tile - s_tp[e];
     const int ct = local / RT, rt = local - ct * RT;
-    const int row0 = s_off[e] + rt * BM;
-    const int nrows = min(BM, cnt - rt * BM);
-    const int col0 = ct * BN;
+    const int row0 = s_off[e] + rt * kTM;
+    const int nrows = min(kTM, cnt - rt * kTM);
+    const int col0 = ct * HC;
 
-    uint32_t a_off[A_LD];
-    int a_dst[A_LD];
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, ch = c & 7;
-      const int rr = (r < nrows) ? r : 0;
-      const int grow = p.a_rows ? p.a_rows[row0 + rr] : (row0 + rr);
-      a_off[i] = (uint32_t)grow * (uint32_t)K + ch * 8;
-      a_dst[i] = swz8(r, ch);
+    // the four source rows (scalars, not an array, so they stay in registers)
+    const uint16_t *src0, *src1, *src2, *src3;
+    {
+      const int r0 = tid >> 2, r1 = r0 + 128;
+      const int g0 = p.a_rows ? p.a_rows[row0 + (r0 < nrows ? r0 : 0)] : row0 + (r0 < nrows ? r0 : 0);
+      const int g1 = p.a_rows ? p.a_rows[row0 + (r1 < nrows ? r1 : 0)] : row0 + (r1 < nrows ? r1 : 0);
+      src0 = p.a + (size_t)g0 * K + lch * 8;
+      src1 = p.a + (size_t)g1 * K + lch * 8;
+      // weight rows r0 and r1 of the tile (gate+up: r1 >= 128 is an up row)
+      const bool up0 = GATEUP && r0 >= HC, up1 = GATEUP && r1 >= HC;
+      int wc0 = col0 + (up0 ? r0 - HC : r0), wc1 = col0 + (up1 ? r1 - HC : r1);
+      if (wc0 >= ncols) wc0 = col0;               // partial column tile
+      if (wc1 >= ncols) wc1 = col0;
+      src2 = (up0 ? p.w1 : p.w0) + ((size_t)e * ncols + wc0) * K + lch * 8;
+      src3 = (up1 ? p.w1 : p.w0) + ((size_t)e * ncols + wc1) * K + lch * 8;
     }
-    const uint16_t* w0 = p.w0 + ((size_t)e * ncols + col0) * K;
-    const uint16_t* w1 = GATEUP ? p.w1 + ((size_t)e * ncols + col0) * K : nullptr;
-    uint32_t b_off[B_LD];
-    int b_dst[B_LD];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, ch = c & 7;
-      const int wr = (GATEUP && r >= BN) ? r - BN : r;
-      b_off[i] = (uint32_t)wr * (uint32_t)K + ch * 8;
-      b_dst[i] = swz8(BM + r, ch);
-    }
-    auto bsrc = [&](int i) -> const uint16_t* {
-      const int r = (tid + 256 * i) >> 3;
-      return ((GATEUP && r >= BN) ? w1 : w0) + b_off[i];
-    };
+#define MOE_LD(PTR, KO) (*reinterpret_cast<const uint4*>((PTR) + (KO)))
 
-    f32x4_t acc[NACC][FM][FN];
+    f32x16_t acc[4][2];
 #pragma unroll
-    for (int g = 0; g < NACC; ++g)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[g][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i)
-      *reinterpret_cast<uint4*>(&lds[a_dst[i]]) = *reinterpret_cast<const uint4*>(p.a + a_off[i]);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      *reinterpret_cast<uint4*>(&lds[b_dst[i]]) = *reinterpret_cast<const uint4*>(bsrc(i));
-    __syncthreads();
+    // prologue: stage 0 into LDS buffer 0, stages 1 and 2 into registers
+    __syncthreads();   // LDS free (previous tile done)
+    *reinterpret_cast<uint4*>(&sbuf[0][ldst[0]]) = MOE_LD(src0, 0);
+    *reinterpret_cast<uint4*>(&sbuf[0][ldst[1]]) = MOE_LD(src1, 0);
+    *reinterpret_cast<uint4*>(&sbuf[0][ldst[2]]) = MOE_LD(src2, 0);
+    *reinterpret_cast<uint4*>(&sbuf[0][ldst[3]]) = MOE_LD(src3, 0);
+    const int k1 = (KT > 1 ? 1 : 0) * kTBK, k2 = (KT > 2 ? 2 : 0) * kTBK;
+    uint4 a10 = MOE_LD(src0, k1), a11 = MOE_LD(src1, k1), a12 = MOE_LD(src2, k1), a13 = MOE_LD(src3, k1);
+    uint4 a20 = MOE_LD(src0, k2), a21 = MOE_LD(src1, k2), a22 = MOE_LD(src2, k2), a23 = MOE_LD(src3, k2);
 
-    const int KT = K / kBK;
     for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      // the last slab re-reads itself so loads/stores stay unconditional
-      const int ko = (kt + 1 < KT ? kt + 1 : kt) * kBK;
-      uint4 ra[A_LD], rb[B_LD];
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const uint4*>(p.a + a_off[i] + ko);
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const uint4*>(bsrc(i) + ko);
-      const uint16_t* L = lds + cur * STAGE;
+      __syncthreads();   // stage kt visible; every wave is done with stage kt-1
+      // stage kt+1 -> the other buffer (read last at stage kt-1); the last
+      // stages re-write valid data so stores stay unconditional
+      uint16_t* Ln = sbuf[(kt + 1) & 1];
+      *reinterpret_cast<uint4*>(&Ln[ldst[0]]) = a10;
+      *reinterpret_cast<uint4*>(&Ln[ldst[1]]) = a11;
+      *reinterpret_cast<uint4*>(&Ln[ldst[2]]) = a12;
+      *reinterpret_cast<uint4*>(&Ln[ldst[3]]) = a13;
+      const int k3 = (kt + 3 < KT ? kt + 3 : KT - 1) * kTBK;
+      a10 = a20; a11 = a21; a12 = a22; a13 = a23;
+      a20 = MOE_LD(src0, k3); a21 = MOE_LD(src1, k3); a22 = MOE_LD(src2, k3); a23 = MOE_LD(src3, k3);
+      const uint16_t* L = sbuf[kt & 1];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int ch = ks * 4 + (lane >> 4);
-        uint4 af[FM];
+        uint4 af[4], bf[2];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const uint4*>(&L[swz8(wm * TM + i * 16 + (lane & 15), ch)]);
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(L + aro[i][ks]);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int rb0 = BM + wn * TN + j * 16 + (lane & 15);
-          const uint4 b0 = *reinterpret_cast<const uint4*>(&L[swz8(rb0, ch)]);
+        for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const uint4*>(L + bro[j][ks]);
 #pragma unroll
-          for (int i = 0; i < FM; ++i) acc[0][i][j] = mfma16(af[i], b0, acc[0][i][j]);
-          if (GATEUP) {
-            const uint4 b1 = *reinterpret_cast<const uint4*>(&L[swz8(rb0 + BN, ch)]);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < FM; ++i) acc[NACC - 1][i][j] = mfma16(af[i], b1, acc[NACC - 1][i][j]);
-          }
-        }
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
       }
-      uint16_t* Ln = lds + (cur ^ 1) * STAGE;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) *reinterpret_cast<uint4*>(&Ln[a_dst[i]]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) *reinterpret_cast<uint4*>(&Ln[b_dst[i]]) = rb[i];
-      __syncthreads();
     }
+#undef MOE_LD
 
+    // ---- epilogue: lane holds column fr of each 32 x 32 block, rows
+    // 8b + 4*fg + q for element 4b + q; 32 lanes store 64 contiguous bytes ----
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wm * TM + i * 16 + (lane >> 4) * 4 + q;
-        if (row >= nrows) continue;
-        const size_t orow = (size_t)(row0 + row) * ncols;
-        const float s = (!GATEUP && p.row_scale) ? p.row_scale[row0 + row] : 1.f;
+      for (int b = 0; b < 4; ++b) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = col0 + wn * TN + j * 16 + (lane & 15);
-          float v;
+        for (int q = 0; q < 4; ++q) {
+          const int row = wm * 128 + 32 * i + 8 * b + 4 * fg + q;
+          if (row >= nrows) continue;
+          uint16_t* orow = p.out + (size_t)(row0 + row) * ncols;
           if (GATEUP) {
-            const float g = acc[0][i][j][q], u = acc[NACC - 1][i][j][q];
-            v = g / (1.f + __expf(-g)) * u;
+            const int col = col0 + wn * 32 + fr;
+            const float g = acc[i][0][4 * b + q], u = acc[i][1][4 * b + q];
+            if (col < ncols) orow[col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
           } else {
-            v = acc[0][i][j][q] * s;
+            const float sc = p.row_scale ? p.row_scale[row0 + row] : 1.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int col = col0 + wn * 64 + 32 * j + fr;
+              if (col < ncols) orow[col] = f32_to_bf16(acc[i][j][4 * b + q] * sc);
+            }
           }
-          p.out[orow + col] = f32_to_bf16(v);
         }
       }
     }
@@ -297,42 +377,35 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(FfnArgs p) {
 
 // ================================ launchers =================================
 
-template <int FM, bool GATEUP>
+template <int FM, bool GATEUP, int LA = 2>
 hipError_t launch_stream(const FfnArgs& a, int num_cu, hipStream_t st) {
   (void)num_cu;
-  const int NT = a.ncols / (4 * kSCols);
+  const int NT = a.ncols / (4 * (GATEUP ? kSCols : 2 * kSCols));
   const long groups = a.E < a.rows_total ? a.E : a.rows_total;   // non-empty groups, at most
-  const long grid = groups * NT;
+  const long passes = a.rows_total / (FM * 16) + groups;          // >= sum of ceil(count / rows per pass)
+  const long grid = passes * NT;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP, LA>), dim3((unsigned)grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
+template <bool GATEUP>
 hipError_t launch_tile(const FfnArgs& a, int num_cu, hipStream_t st) {
-  constexpr int NB = GATEUP ? 2 * BN : BN;
-  const size_t lds = (size_t)2 * (BM + NB) * kBK * sizeof(uint16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_tile_kernel<BM, BN, WM, WN, GATEUP>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int NT = a.ncols / BN;
-  const long ub_rows = a.rows_total / BM + (a.E < a.rows_total ? a.E : a.rows_total);
+  constexpr int HC = GATEUP ? kTN / 2 : kTN;
+  const int NT = ceil_div(a.ncols, HC);
+  const long ub_rows = a.rows_total / kTM + (a.E < a.rows_total ? a.E : a.rows_total);
   const long ub = ub_rows * NT;
-  long grid = num_cu;
+  long grid = (num_cu / 8) * 8;
   if (ub < grid) grid = ((ub + 7) / 8) * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_tile_kernel<BM, BN, WM, WN, GATEUP>), dim3((unsigned)grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP>), dim3((unsigned)grid), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
 // Mean rows per group decides the kernel; the streaming kernel's pass height
 // covers ~1.5x the mean so that typical groups take one pass.
-int stream_fm(const FfnArgs& a) {
-  if (a.K % kSK != 0 || a.ncols % (4 * kSCols) != 0) return 0;
+int stream_fm(const FfnArgs& a, bool gateup) {
+  if (a.K % kSK != 0 || a.ncols % (4 * kSCols * (gateup ? 1 : 2)) != 0) return 0;
   const double mean = (double)a.rows_total / (a.E > 0 ? a.E : 1);
   if (mean > 56.0) return 0;
   const double need = mean * 1.2;
@@ -346,28 +419,26 @@ int stream_fm(const FfnArgs& a) {
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st) {
   if (a.rows_total == 0) return hipSuccess;
-  switch (stream_fm(a)) {
+  switch (stream_fm(a, true)) {
     case 1: return launch_stream<1, true>(a, num_cu, st);
     case 2: return launch_stream<2, true>(a, num_cu, st);
     case 3: return launch_stream<3, true>(a, num_cu, st);
     case 4: return launch_stream<4, true>(a, num_cu, st);
     default: break;
   }
-  if (a.ncols % 128 == 0) return launch_tile<256, 128, 2, 2, true>(a, num_cu, st);
-  return launch_tile<128, 64, 2, 2, true>(a, num_cu, st);
+  return launch_tile<true>(a, num_cu, st);
 }
 
 hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st) {
   if (a.rows_total == 0) return hipSuccess;
-  switch (stream_fm(a)) {
+  switch (stream_fm(a, false)) {
     case 1: return launch_stream<1, false>(a, num_cu, st);
     case 2: return launch_stream<2, false>(a, num_cu, st);
     case 3: return launch_stream<3, false>(a, num_cu, st);
     case 4: return launch_stream<4, false>(a, num_cu, st);
     default: break;
   }
-  if (a.ncols % 256 == 0) return launch_tile<256, 256, 2, 2, false>(a, num_cu, st);
-  return launch_tile<128, 64, 2, 2, false>(a, num_cu, st);
+  return launch_tile<false>(a, num_cu, st);
 }
 
 }  // namespace moe

@@ -10,7 +10,7 @@ constexpr int kMaxGroups = 256;
 // Loads the group offsets into LDS and forms the inclusive prefix of tiles:
 // tprefix[e+1] = sum_{g<=e} tiles(g), tiles(g) = row_tiles(count_g) * col_tiles.
 // Row tiles of an empty group are 0, so empty experts never appear.  Must be
-// called by all 256 threads of the block.
+// called by every thread of the block (blockDim.x >= 256).
 template <int ROWS_PER_TILE>
 __device__ __forceinline__ int build_tile_list(const FfnArgs& p, int col_tiles, int* s_off, int* s_tp) {
   const int tid = threadIdx.x;
@@ -28,7 +28,7 @@ __device__ __forceinline__ int build_tile_list(const FfnArgs& p, int col_tiles, 
     const int cnt = s_off[tid + 1] - s_off[tid];
     tv = (ROWS_PER_TILE > 0 ? ceil_div(cnt, ROWS_PER_TILE) : (cnt > 0 ? 1 : 0)) * col_tiles;
   }
-  if (tid < kMaxGroups) s_tp[tid + 1] = tv;
+  if (tid < kMaxGroups) s_tp[tid + 1] = tv;   // groups beyond E contribute 0
   if (tid == 0) s_tp[0] = 0;
   __syncthreads();
   for (int off = 1; off < kMaxGroups; off <<= 1) {

@@ -104,6 +104,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     const int e = lane + 64 * i;
     float s = 0.f;
     if (e < E) {
+#pragma unroll 8
       for (int ks = 0; ks < KS; ++ks) s += part[((size_t)ks * N + n) * EP + e];
       if (bias) s += bias[e];
     }
