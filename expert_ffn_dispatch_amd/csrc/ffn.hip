@@ -315,35 +315,39 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     *reinterpret_cast<uint4*>(&sbuf[0][ldst[2]]) = MOE_LD(src2, 0);
     *reinterpret_cast<uint4*>(&sbuf[0][ldst[3]]) = MOE_LD(src3, 0);
     const int k1 = (KT > 1 ? 1 : 0) * kTBK, k2 = (KT > 2 ? 2 : 0) * kTBK;
-    uint4 a10 = MOE_LD(src0, k1), a11 = MOE_LD(src1, k1), a12 = MOE_LD(src2, k1), a13 = MOE_LD(src3, k1);
-    uint4 a20 = MOE_LD(src0, k2), a21 = MOE_LD(src1, k2), a22 = MOE_LD(src2, k2), a23 = MOE_LD(src3, k2);
+    // two register sets take turns (no copies, which would force a wait on
+    // the newer loads): at stage kt the set holding stage kt+1 is written to
+    // LDS and refilled with stage kt+3
+    uint4 x0 = MOE_LD(src0, k1), x1 = MOE_LD(src1, k1), x2 = MOE_LD(src2, k1), x3 = MOE_LD(src3, k1);
+    uint4 y0 = MOE_LD(src0, k2), y1 = MOE_LD(src1, k2), y2 = MOE_LD(src2, k2), y3 = MOE_LD(src3, k2);
 
-    for (int kt = 0; kt < KT; ++kt) {
-      __syncthreads();   // stage kt visible; every wave is done with stage kt-1
-      // stage kt+1 -> the other buffer (read last at stage kt-1); the last
-      // stages re-write valid data so stores stay unconditional
-      uint16_t* Ln = sbuf[(kt + 1) & 1];
-      *reinterpret_cast<uint4*>(&Ln[ldst[0]]) = a10;
-      *reinterpret_cast<uint4*>(&Ln[ldst[1]]) = a11;
-      *reinterpret_cast<uint4*>(&Ln[ldst[2]]) = a12;
-      *reinterpret_cast<uint4*>(&Ln[ldst[3]]) = a13;
-      const int k3 = (kt + 3 < KT ? kt + 3 : KT - 1) * kTBK;
-      a10 = a20; a11 = a21; a12 = a22; a13 = a23;
-      a20 = MOE_LD(src0, k3); a21 = MOE_LD(src1, k3); a22 = MOE_LD(src2, k3); a23 = MOE_LD(src3, k3);
-      const uint16_t* L = sbuf[kt & 1];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4 af[4], bf[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(L + aro[i][ks]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const uint4*>(L + bro[j][ks]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
-      }
+#define MOE_KSTEP(KT_, R0, R1, R2, R3)                                                            \
+    do {                                                                                          \
+      __syncthreads();   /* stage KT_ visible; every wave is done with stage KT_-1 */             \
+      /* stage KT_+1 -> the other buffer (read last at stage KT_-1); the last */                  \
+      /* stages re-write valid data so stores stay unconditional */                               \
+      uint16_t* Ln_ = sbuf[((KT_) + 1) & 1];                                                      \
+      *reinterpret_cast<uint4*>(&Ln_[ldst[0]]) = R0;                                              \
+      *reinterpret_cast<uint4*>(&Ln_[ldst[1]]) = R1;                                              \
+      *reinterpret_cast<uint4*>(&Ln_[ldst[2]]) = R2;                                              \
+      *reinterpret_cast<uint4*>(&Ln_[ldst[3]]) = R3;                                              \
+      const int k3_ = ((KT_) + 3 < KT ? (KT_) + 3 : KT - 1) * kTBK;                               \
+      R0 = MOE_LD(src0, k3_); R1 = MOE_LD(src1, k3_); R2 = MOE_LD(src2, k3_); R3 = MOE_LD(src3, k3_); \
+      const uint16_t* L_ = sbuf[(KT_) & 1];                                                       \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                          \
+        uint4 af[4], bf[2];                                                                       \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(L_ + aro[i][ks]); \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const uint4*>(L_ + bro[j][ks]); \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                             \
+          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]); \
+      }                                                                                           \
+    } while (0)
+
+    for (int kt = 0; kt < KT; kt += 2) {
+      MOE_KSTEP(kt, x0, x1, x2, x3);
+      if (kt + 1 < KT) MOE_KSTEP(kt + 1, y0, y1, y2, y3);
     }
+#undef MOE_KSTEP
 #undef MOE_LD
 
     // ---- epilogue: lane holds column fr of each 32 x 32 block, rows
