@@ -78,6 +78,9 @@ def main() -> int:
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--tokens", type=int, default=None, help="token count for the decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30,
+                    help="size of the plain device copy timed after the layer (0 = skip); its GB/s is "
+                         "the practical bandwidth ceiling and its counters scale FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--flush", action="store_true",
                     help="overwrite a 1 GiB buffer before every step (outside the per-step events) "
                          "so weights are read from HBM, and report the event-timed layer")
@@ -89,6 +92,7 @@ def main() -> int:
 
     import torch
     import expert_ffn_dispatch_amd as moe
+    from expert_ffn_dispatch_amd import profiling
     from datagen import configs, gen
 
     w = configs.get(args.workload, args.tokens)
@@ -154,7 +158,11 @@ def main() -> int:
     F, B = layer_work(w, active)
     Fg, Bg = gateup_work(w, active)
     t_gu = stage_ms[:, 3].mean() * 1e-3
-    achieved = Bg / t_gu / 1e9
+    # the gate+up launch is bound by MFMA when its flops per algorithmic
+    # byte exceed the ridge point (peak flops / peak bandwidth), else by HBM
+    mfma_bound = Fg / Bg > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    achieved = Fg / t_gu / 1e12 if mfma_bound else Bg / t_gu / 1e9
+    peak = BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS
     t_layer = ms_per_step * 1e-3
     t_roof = max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9))
     res = {
@@ -164,9 +172,12 @@ def main() -> int:
         "config": {"workload": w.title, "N": w.N, "M": w.M, "E": w.E, "k": w.k, "H": w.H, "S": w.S, "Hs": w.Hs,
                    "parallelism": "single GPU", "timing": "event-timed, caches flushed" if args.flush
                    else "wall clock over back-to-back steps"},
-        "roofline": {"bound": "hbm", "kernel": "ffn_kernel gate+up (grouped SwiGLU phase 1)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": Bg, "avg_us": t_gu * 1e6},
+        "roofline": {"bound": "mfma" if mfma_bound else "hbm",
+                     "kernel": "grouped SwiGLU gate+up GEMM (ffn_stream_kernel at decode-sized experts, "
+                               "ffn_tile_kernel otherwise)",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                     "frac": achieved / peak, "traffic": None, "algorithmic_bytes": Bg, "algorithmic_flops": Fg,
+                     "avg_us": t_gu * 1e6},
         "layer": {"flops": F, "bytes": B, "tflops": F / t_layer / 1e12, "hbm_gbs": B / t_layer / 1e9,
                   "mfma_frac": F / t_layer / (BF16_PEAK_TFLOPS * 1e12), "hbm_frac": B / t_layer / (HBM_PEAK_GBS * 1e9),
                   "roofline_frac": t_roof / t_layer, "t_roof_us": t_roof * 1e6,
@@ -175,6 +186,24 @@ def main() -> int:
         "routing": {"active_experts": active, "max_rows": int(counts.max()), "mean_rows": float(counts.mean()),
                     "empty_experts": int((counts == 0).sum())},
     }
+    if args.copy_bytes > 0:
+        # a plain elementwise copy of known size: reads and writes copy_bytes
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.add(src, 0.0, out=dst)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            torch.add(src, 0.0, out=dst)
+        c1.record()
+        torch.cuda.synchronize()
+        res["copy_gbs"] = 2.0 * n * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{w.name}_N{w.N}.txt"))
+    if tr is not None:
+        res["roofline"]["traffic"] = float(tr["traffic_bytes"])
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, d)
