@@ -343,9 +343,12 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
       }                                                                                           \
     } while (0)
 
+    // K % 64 == 0 (checked at the boundary), so KT is even and both steps
+    // of an iteration always run (a conditional second step would make the
+    // compiler wait for every load in flight at the loop head)
     for (int kt = 0; kt < KT; kt += 2) {
       MOE_KSTEP(kt, x0, x1, x2, x3);
-      if (kt + 1 < KT) MOE_KSTEP(kt + 1, y0, y1, y2, y3);
+      MOE_KSTEP(kt + 1, y0, y1, y2, y3);
     }
 #undef MOE_KSTEP
 #undef MOE_LD
