@@ -198,6 +198,150 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
   }
 }
 
+// Decode variant (at most 16 rows per pass): the four waves of a block share
+// one 16-row x WCOLS output tile and split the contraction four ways, so a
+// batch of a few tokens still spreads over hundreds of blocks.  Each wave
+// stages its own token rows and weight rows in private LDS slots, so the k
+// loop has no block barrier; the four partial tiles are summed in wave order
+// through LDS at the end (deterministic).
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
+  constexpr int RB = 16;
+  constexpr int WCOLS = GATEUP ? kSCols : 2 * kSCols;   // output columns per block
+  constexpr int LA = 2;
+  __shared__ __align__(16) uint16_t sa[4][RB * kSK];
+  __shared__ __align__(16) uint16_t sb[4][2][kSCols * kSK];
+  __shared__ int s_off[kMaxGroups + 1];
+  __shared__ int s_tp[kMaxGroups + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.K, ncols = p.ncols;
+  const int NT = ncols / WCOLS;
+  const int NC = K / kSK;                     // the host sends only K % 128 == 0 here
+  const int c0 = (wave * NC) / 4, c1 = ((wave + 1) * NC) / 4;   // this wave's chunks
+  const int total = build_tile_list<RB>(p, NT, s_off, s_tp);
+  const int tile = blockIdx.x;
+  if (tile >= total) return;
+  const int e = find_group(s_tp, p.E, tile);
+  const int cnt = s_off[e + 1] - s_off[e];
+  const int RT = ceil_div(cnt, RB);
+  const int local = tile - s_tp[e];
+  const int ct = local / RT, rt = local - ct * RT;
+  const int row0 = s_off[e] + rt * RB;
+  const int nrows = min(RB, cnt - rt * RB);
+  const int col0 = ct * WCOLS;
+
+  const int brow = lane >> 4, bch = lane & 15, fr = lane & 15;
+  const size_t wrow = ((size_t)e * ncols + col0 + brow) * K + bch * 8;
+  const uint16_t* wb0 = p.w0 + wrow;
+  const uint16_t* wb1 = GATEUP ? p.w1 + wrow : p.w0 + wrow + (size_t)kSCols * K;
+  int bdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + brow;
+    bdst[i] = r * kSK + ((bch ^ r) << 3);
+  }
+  // token rows: lane loads rows 4i + (lane >> 4), chunk lane & 15 (like the weights)
+  uint32_t aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + brow;
+    const int rr = (r < nrows) ? r : 0;
+    const int grow = p.a_rows ? p.a_rows[row0 + rr] : (row0 + rr);
+    aoff[i] = (uint32_t)grow * (uint32_t)K + bch * 8;
+  }
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+
+  if (c0 < c1) {
+    // prologue: chunk c0 into LDS, c0+1..c0+LA into registers
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ko = c0 * kSK;
+      *reinterpret_cast<uint4*>(&sa[wave][bdst[i]]) = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ko);
+      *reinterpret_cast<uint4*>(&sb[wave][0][bdst[i]]) = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K + ko);
+      *reinterpret_cast<uint4*>(&sb[wave][1][bdst[i]]) = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K + ko);
+    }
+    uint4 qa[LA][4], qb[LA][2][4];
+#pragma unroll
+    for (int l = 0; l < LA; ++l) {
+      const int ko = min(c0 + 1 + l, c1 - 1) * kSK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qa[l][i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ko);
+        qb[l][0][i] = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K + ko);
+        qb[l][1][i] = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K + ko);
+      }
+    }
+    for (int c = c0; c < c1; ++c) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int ch = s * 4 + (lane >> 4);
+        const int off = fr * kSK + ((ch ^ fr) << 3);
+        const uint4 af = *reinterpret_cast<const uint4*>(&sa[wave][off]);
+        acc0 = mfma16(af, *reinterpret_cast<const uint4*>(&sb[wave][0][off]), acc0);
+        acc1 = mfma16(af, *reinterpret_cast<const uint4*>(&sb[wave][1][off]), acc1);
+      }
+      // same wave: LDS operations complete in order, so the slot can be
+      // overwritten right after this wave's reads
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint4*>(&sa[wave][bdst[i]]) = qa[0][i];
+        *reinterpret_cast<uint4*>(&sb[wave][0][bdst[i]]) = qb[0][0][i];
+        *reinterpret_cast<uint4*>(&sb[wave][1][bdst[i]]) = qb[0][1][i];
+      }
+#pragma unroll
+      for (int l = 0; l + 1 < LA; ++l)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qa[l][i] = qa[l + 1][i];
+          qb[l][0][i] = qb[l + 1][0][i];
+          qb[l][1][i] = qb[l + 1][1][i];
+        }
+      const int ko = min(c + 1 + LA, c1 - 1) * kSK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qa[LA - 1][i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ko);
+        qb[LA - 1][0][i] = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K + ko);
+        qb[LA - 1][1][i] = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K + ko);
+      }
+    }
+  }
+
+  // partial tiles -> LDS (reusing the weight slots), summed in wave order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&sb[0][0][0]);   // [4 waves][64 lanes][8]
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    red[(wave * 64 + lane) * 8 + q] = acc0[q];
+    red[(wave * 64 + lane) * 8 + 4 + q] = acc1[q];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = red[lane * 8 + q];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += red[(w * 64 + lane) * 8 + q];
+    const int col = col0 + fr;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = (lane >> 4) * 4 + q;
+      if (r >= nrows) continue;
+      const int orow = row0 + r;
+      if (GATEUP) {
+        const float g = v[q], u = v[4 + q];
+        p.out[(size_t)orow * ncols + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+      } else {
+        const float sc = p.row_scale ? p.row_scale[orow] : 1.f;
+        p.out[(size_t)orow * ncols + col] = f32_to_bf16(v[q] * sc);
+        p.out[(size_t)orow * ncols + col + kSCols] = f32_to_bf16(v[4 + q] * sc);
+      }
+    }
+  }
+}
+
 // ============================== tiled kernel ===============================
 //
 // 256 rows x 256 weight rows per tile (gate+up: 128 gate and the same 128 up
@@ -409,6 +553,25 @@ hipError_t launch_tile(const FfnArgs& a, int num_cu, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The split-contraction decode kernel pays off only when the plain streaming
+// launch would have too few blocks to keep every CU streaming (measured: it
+// helps a 1-token batch, and loses at 32 tokens).
+bool use_split_waves(const FfnArgs& a, bool gateup) {
+  const long groups = a.E < a.rows_total ? a.E : a.rows_total;
+  const long blocks = groups * (a.ncols / (4 * kSCols * (gateup ? 1 : 2)));
+  return blocks < 1024;
+}
+
+template <bool GATEUP>
+hipError_t launch_stream_ks(const FfnArgs& a, hipStream_t st) {
+  const int NT = a.ncols / (GATEUP ? kSCols : 2 * kSCols);
+  const long groups = a.E < a.rows_total ? a.E : a.rows_total;
+  const long grid = (a.rows_total / 16 + groups) * NT;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((ffn_stream_ks_kernel<GATEUP>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // Mean rows per group decides the kernel; the streaming kernel's pass height
 // covers ~1.5x the mean so that typical groups take one pass.
 int stream_fm(const FfnArgs& a, bool gateup) {
@@ -427,7 +590,7 @@ int stream_fm(const FfnArgs& a, bool gateup) {
 hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st) {
   if (a.rows_total == 0) return hipSuccess;
   switch (stream_fm(a, true)) {
-    case 1: return launch_stream<1, true>(a, num_cu, st);
+    case 1: return use_split_waves(a, true) ? launch_stream_ks<true>(a, st) : launch_stream<1, true>(a, num_cu, st);
     case 2: return launch_stream<2, true>(a, num_cu, st);
     case 3: return launch_stream<3, true>(a, num_cu, st);
     case 4: return launch_stream<4, true>(a, num_cu, st);
@@ -439,7 +602,7 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st) {
 hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st) {
   if (a.rows_total == 0) return hipSuccess;
   switch (stream_fm(a, false)) {
-    case 1: return launch_stream<1, false>(a, num_cu, st);
+    case 1: return use_split_waves(a, false) ? launch_stream_ks<false>(a, st) : launch_stream<1, false>(a, num_cu, st);
     case 2: return launch_stream<2, false>(a, num_cu, st);
     case 3: return launch_stream<3, false>(a, num_cu, st);
     case 4: return launch_stream<4, false>(a, num_cu, st);
