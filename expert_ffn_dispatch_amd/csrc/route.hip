@@ -12,7 +12,7 @@
 // Three launches:
 //   transpose - W_r [M][E] -> W_rT [EP][M] (E padded to 16), so that both MFMA
 //               operands read 16 contiguous bytes of the contraction per lane
-//   logits    - one wave per (16 tokens, k slice): partial scores for all
+//   logits    - one wave per (16-64 tokens, k slice): partial scores for all
 //               experts; the contraction is split into KS slices so that even
 //               a decode batch spreads over hundreds of waves
 //   topk      - one wave per token: sums the KS partials in slice order
@@ -43,51 +43,53 @@ __global__ __launch_bounds__(256) void router_transpose_kernel(const uint16_t* _
   }
 }
 
-// part[ks][n][e] = sum over the slice's k of x[n,k] * W_r[k,e]
-template <int NCB>
+// part[ks][n][e] = sum over the slice's k of x[n,k] * W_r[k,e].  One wave
+// covers RW x 16 tokens and all experts for one k slice, so each router
+// fragment it loads serves RW token blocks.
+template <int NCB, int RW>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ wt, int N, int M,
                                                             int steps_per_slice, float* __restrict__ part) {
   constexpr int EP = NCB * 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tg = blockIdx.x * 4 + wave;
-  const int tok0 = tg * 16;
+  const int tok0 = tg * 16 * RW;
   if (tok0 >= N) return;
   const int ks = blockIdx.y;
   const int s0 = ks * steps_per_slice;
   const int s1 = min(M / 32, s0 + steps_per_slice);
   const int r = lane & 15, g = lane >> 4;
-  const int tok = min(tok0 + r, N - 1);
-  const uint16_t* xa = x + (size_t)tok * M + g * 8;
+  const uint16_t* xa[RW];
+#pragma unroll
+  for (int t = 0; t < RW; ++t) xa[t] = x + (size_t)min(tok0 + 16 * t + r, N - 1) * M + g * 8;
   const uint16_t* wb = wt + (size_t)r * M + g * 8;
 
-  f32x4_t acc[NCB];
+  f32x4_t acc[RW][NCB];
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 a = *reinterpret_cast<const uint4*>(xa + s0 * 32);
-  uint4 b[NCB];
+  for (int t = 0; t < RW; ++t)
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) b[c] = *reinterpret_cast<const uint4*>(wb + (size_t)c * 16 * M + s0 * 32);
+    for (int c = 0; c < NCB; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s = s0; s < s1; ++s) {
-    const int sn = (s + 1 < s1) ? s + 1 : s;
-    const uint4 an = *reinterpret_cast<const uint4*>(xa + sn * 32);
-    uint4 bn[NCB];
+    uint4 a[RW], b[NCB];
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) bn[c] = *reinterpret_cast<const uint4*>(wb + (size_t)c * 16 * M + sn * 32);
+    for (int t = 0; t < RW; ++t) a[t] = *reinterpret_cast<const uint4*>(xa[t] + s * 32);
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) acc[c] = mfma16(a, b[c], acc[c]);
-    a = an;
+    for (int c = 0; c < NCB; ++c) b[c] = *reinterpret_cast<const uint4*>(wb + (size_t)c * 16 * M + s * 32);
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) b[c] = bn[c];
+    for (int t = 0; t < RW; ++t)
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) acc[t][c] = mfma16(a[t], b[c], acc[t][c]);
   }
   float* out = part + (size_t)ks * N * EP;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int n = tok0 + g * 4 + q;
-    if (n >= N) continue;
+  for (int t = 0; t < RW; ++t)
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) out[(size_t)n * EP + c * 16 + r] = acc[c][q];
-  }
+    for (int q = 0; q < 4; ++q) {
+      const int n = tok0 + 16 * t + g * 4 + q;
+      if (n >= N) continue;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) out[(size_t)n * EP + c * 16 + r] = acc[t][c][q];
+    }
 }
 
 template <int PER>
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 }
 
 struct RoutePlan {
-  int NCB, EP, KS, steps;
+  int NCB, EP, RW, KS, steps;
 };
 
 RoutePlan plan(int N, int M, int E) {
@@ -153,21 +155,33 @@ RoutePlan plan(int N, int M, int E) {
   const int ncb = ceil_div(E, 16);
   p.NCB = ncb <= 1 ? 1 : ncb <= 2 ? 2 : ncb <= 4 ? 4 : ncb <= 8 ? 8 : ncb <= 10 ? 10 : ncb <= 12 ? 12 : 16;
   p.EP = p.NCB * 16;
-  const int tg = ceil_div(N, 16);
+  // tokens per wave: more rows reuse each router fragment, fewer rows spread
+  // a small batch over more waves
+  p.RW = (N >= 2048 && p.NCB <= 8) ? 4 : (N >= 512 ? 2 : 1);
+  const int waves = ceil_div(N, 16 * p.RW);
   const int total_steps = M / 32;
-  int ks = ceil_div(2048, tg);
+  int ks = ceil_div(2048, waves);
   const int max_ks = ceil_div(total_steps, 4);      // slices of at least 128 k
   if (ks > max_ks) ks = max_ks;
+  // partial scores are written and re-read once: keep them small
+  while (ks > 1 && (size_t)ks * N * p.EP * 4 > ((size_t)16 << 20)) --ks;
   if (ks < 1) ks = 1;
   p.steps = ceil_div(total_steps, ks);
   p.KS = ceil_div(total_steps, p.steps);
   return p;
 }
 
+template <int NCB, int RW>
+void launch_logits_rw(const RouteArgs& a, const RoutePlan& pl, const uint16_t* wt, float* part, hipStream_t st) {
+  hipLaunchKernelGGL((router_logits_kernel<NCB, RW>), dim3(ceil_div(a.N, 64 * RW), pl.KS), dim3(256), 0, st, a.x,
+                     wt, a.N, a.M, pl.steps, part);
+}
+
 template <int NCB>
 void launch_logits(const RouteArgs& a, const RoutePlan& pl, const uint16_t* wt, float* part, hipStream_t st) {
-  hipLaunchKernelGGL((router_logits_kernel<NCB>), dim3(ceil_div(a.N, 64), pl.KS), dim3(256), 0, st, a.x, wt,
-                     a.N, a.M, pl.steps, part);
+  if (pl.RW == 4) launch_logits_rw<NCB, (NCB <= 8 ? 4 : 2)>(a, pl, wt, part, st);
+  else if (pl.RW == 2) launch_logits_rw<NCB, 2>(a, pl, wt, part, st);
+  else launch_logits_rw<NCB, 1>(a, pl, wt, part, st);
 }
 
 }  // namespace
