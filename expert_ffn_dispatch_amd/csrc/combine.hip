@@ -23,19 +23,37 @@ __device__ __forceinline__ void add8(float (&acc)[8], uint4 v, float w) {
   }
 }
 
-// One block per token row; each thread owns 16-byte chunks of the row.
+// One block per token row; each thread owns 16-byte chunks of the row.  The
+// token's k positions and weights are read once; per chunk all k expert rows
+// are loaded before the first is summed (KM >= k slots, unrolled).
+template <int KM>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs p) {
   const int n = blockIdx.x;
   const int chunks = p.M >> 3;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < p.k; ++j) {
-      const int a = n * p.k + j;
-      const int pos = p.a2s[a];
-      const float w = p.weights ? p.weights[a] : 1.f;
-      add8(acc, *reinterpret_cast<const uint4*>(p.y + (size_t)pos * p.M + c * 8), w);
+  const int k = p.k;
+  int pos[KM];
+  float w[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    pos[j] = 0;
+    w[j] = 0.f;
+    if (j < k) {
+      pos[j] = p.a2s[n * k + j];
+      w[j] = p.weights ? p.weights[n * k + j] : 1.f;
     }
-    if (p.shared) add8(acc, *reinterpret_cast<const uint4*>(p.shared + (size_t)n * p.M + c * 8), 1.f);
+  }
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    uint4 v[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) v[j] = *reinterpret_cast<const uint4*>(p.y + (size_t)pos[j] * p.M + c * 8);
+    uint4 sv = make_uint4(0, 0, 0, 0);
+    if (p.shared) sv = *reinterpret_cast<const uint4*>(p.shared + (size_t)n * p.M + c * 8);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) add8(acc, v[j], w[j]);
+    if (p.shared) add8(acc, sv, 1.f);
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
     o.y = pack_bf16x2(acc[2], acc[3]);
@@ -49,7 +67,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs p) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.N), dim3(256), 0, st, a);
+  const dim3 g(a.N), b(256);
+  if (a.k <= 1) hipLaunchKernelGGL(combine_kernel<1>, g, b, 0, st, a);
+  else if (a.k <= 2) hipLaunchKernelGGL(combine_kernel<2>, g, b, 0, st, a);
+  else if (a.k <= 4) hipLaunchKernelGGL(combine_kernel<4>, g, b, 0, st, a);
+  else if (a.k <= 8) hipLaunchKernelGGL(combine_kernel<8>, g, b, 0, st, a);
+  else hipLaunchKernelGGL(combine_kernel<16>, g, b, 0, st, a);
   return hipGetLastError();
 }
 

@@ -16,6 +16,9 @@
 //             (lanes with the same expert and a lower lane id) plus the
 //             counts of earlier waves, so sorted slot =
 //             offsets[e] + tile_off[e][t] + rank.
+// A batch of at most kSmallPermute assignments takes one launch instead: a
+// single block counts, scans and then ranks the assignments 1024 at a time,
+// carrying each expert's running count across the chunks in LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -116,6 +119,87 @@ __global__ __launch_bounds__(256) void scatter_kernel(PermuteArgs p, int T, int 
   }
 }
 
+constexpr int kSmallPermute = 4096;
+
+// The same dispatch and stable permutation for a small batch, in one block of
+// 16 waves: LDS histogram, one-wave scan of the counts, then chunks of 1024
+// assignments in index order, each ranked like the scatter kernel's tiles.
+__global__ __launch_bounds__(1024) void permute_small_kernel(PermuteArgs p, int nbits) {
+  __shared__ int cnt[256];
+  __shared__ int base[256];     // assignments of each expert placed by earlier chunks
+  __shared__ int off_s[256];
+  __shared__ int wc[16][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.E, A = p.A;
+  if (tid < E) {
+    cnt[tid] = 0;
+    base[tid] = 0;
+  }
+  __syncthreads();
+  for (int a = tid; a < A; a += 1024) atomicAdd(&cnt[clamp_expert(p.ids[a], E)], 1);
+  __syncthreads();
+  if (wave == 0) {
+    int v[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      v[i] = (e < E) ? cnt[e] : 0;
+      s += v[i];
+    }
+    int inc = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    int b = inc - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      if (e < E) {
+        p.counts[e] = v[i];
+        p.offsets[e] = b;
+        off_s[e] = b;
+      }
+      b += v[i];
+    }
+    if (lane == 63) p.offsets[E] = inc;
+  }
+  for (int t0 = 0; t0 < A; t0 += 1024) {
+    for (int i = tid; i < 16 * 256; i += 1024) (&wc[0][0])[i] = 0;
+    __syncthreads();
+    const int a = t0 + tid;
+    const bool valid = a < A;
+    const int e = valid ? clamp_expert(p.ids[a], E) : 0;
+    uint64_t peers = __ballot(valid);
+    for (int bt = 0; bt < nbits; ++bt) {
+      const bool bit = (e >> bt) & 1;
+      const uint64_t m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = lanes_below(peers);
+    if (valid && rank == 0) wc[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int before = base[e];
+      for (int w = 0; w < wave; ++w) before += wc[w][e];
+      const int pos = off_s[e] + before + rank;
+      p.s2a[pos] = a;
+      p.a2s[a] = pos;
+      if (p.row_token) p.row_token[pos] = a / p.k;
+      if (p.row_weight) p.row_weight[pos] = p.weights[a];
+    }
+    __syncthreads();
+    if (tid < E) {
+      int s = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) s += wc[w][tid];
+      base[tid] += s;
+    }
+    __syncthreads();            // wc is cleared again by the next chunk
+  }
+}
+
 // Row copy: one block moves `rows` rows of M bf16 in 16-byte chunks.
 __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ x,
                                                      const int32_t* __restrict__ s2a, int k, int A,
@@ -139,6 +223,10 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   const int T = ceil_div(a.A, kPermTile);
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
+  if (a.A <= kSmallPermute) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, a, nbits);
+    return hipGetLastError();
+  }
   if (T > 0) {
     hipLaunchKernelGGL(hist_kernel, dim3(T), dim3(256), 0, st, a.ids, a.A, a.E, T, a.tile_hist);
   }

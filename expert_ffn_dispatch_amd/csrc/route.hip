@@ -30,13 +30,23 @@ __global__ __launch_bounds__(256) void router_transpose_kernel(const uint16_t* _
   __shared__ uint16_t t[64][66];
   const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
-  for (int i = tid; i < 64 * 64; i += 256) {
-    const int kk = i >> 6, ee = i & 63;
-    const int e = e0 + ee;
-    t[kk][ee] = (e < E) ? wr[(size_t)(k0 + kk) * E + e] : 0;
+  // all sixteen loads of a thread are issued before the first LDS store
+  uint16_t v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = tid + 256 * j;
+    const int e = e0 + (i & 63);
+    v[j] = (e < E) ? wr[(size_t)(k0 + (i >> 6)) * E + e] : (uint16_t)0;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = tid + 256 * j;
+    t[i >> 6][i & 63] = v[j];
   }
   __syncthreads();
-  for (int i = tid; i < 64 * 64; i += 256) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = tid + 256 * j;
     const int ee = i >> 6, kk = i & 63;
     const int e = e0 + ee;
     if (e < EP) wt[(size_t)e * M + k0 + kk] = t[kk][ee];

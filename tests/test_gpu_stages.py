@@ -60,6 +60,27 @@ def test_permute_bit_exact(shape):
     assert np.array_equal(host_bits(g["x_sorted"]), O.gather(d["x"], o["sorted_to_assign"], dm.top_k))
 
 
+# Both launch shapes of the permutation: one block up to 4096 assignments,
+# tiles of 256 beyond; ragged last tile, more experts than a tile holds.
+PERMUTE_SIZES = [(1024, 64, 4), (4097, 16, 1), (2500, 256, 8), (3000, 3, 2), (1, 1, 1)]
+
+
+@pytest.mark.parametrize("size", PERMUTE_SIZES, ids=[str(s) for s in PERMUTE_SIZES])
+def test_permute_launch_shapes(size):
+    N, E, k = size
+    note(f"permute sizes N={N} E={E} k={k}")
+    rng = np.random.default_rng(N * 1000 + E)
+    # skewed expert choice: a few hot experts and empty ones
+    pop = rng.zipf(1.5, size=(N, k)) % E
+    ids = pop.astype(np.int32)
+    dm = moe.dims(N, 64, E, k, 64)
+    g = moe.moe_permute(dm, i32(ids))
+    torch.cuda.synchronize()
+    o = O.dispatch(ids, E)
+    for key in ("expert_counts", "expert_offsets", "sorted_to_assign", "assign_to_sorted"):
+        assert np.array_equal(g[key].cpu().numpy(), o[key]), key
+
+
 def test_permute_forced_and_empty():
     """All assignments on one expert except the k-1 others forced per token."""
     N, E, k = 1000, 32, 3
