@@ -125,6 +125,7 @@ constexpr int kSmallPermute = 4096;
 // 16 waves: LDS histogram, one-wave scan of the counts, then chunks of 1024
 // assignments in index order, each ranked like the scatter kernel's tiles.
 __global__ __launch_bounds__(1024) void permute_small_kernel(PermuteArgs p, int nbits) {
+  constexpr int kChunks = kSmallPermute / 1024;
   __shared__ int cnt[256];
   __shared__ int base[256];     // assignments of each expert placed by earlier chunks
   __shared__ int off_s[256];
@@ -135,8 +136,19 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(PermuteArgs p, int 
     cnt[tid] = 0;
     base[tid] = 0;
   }
+  // every assignment's expert (and weight) is read once, into registers
+  int ev[kChunks];
+  float wv[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int a = c * 1024 + tid;
+    ev[c] = (a < A) ? clamp_expert(p.ids[a], E) : 0;
+    wv[c] = (a < A && p.row_weight) ? p.weights[a] : 0.f;
+  }
   __syncthreads();
-  for (int a = tid; a < A; a += 1024) atomicAdd(&cnt[clamp_expert(p.ids[a], E)], 1);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    if (c * 1024 + tid < A) atomicAdd(&cnt[ev[c]], 1);
   __syncthreads();
   if (wave == 0) {
     int v[4], s = 0;
@@ -165,12 +177,14 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(PermuteArgs p, int 
     }
     if (lane == 63) p.offsets[E] = inc;
   }
-  for (int t0 = 0; t0 < A; t0 += 1024) {
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    if (c * 1024 >= A) break;   // uniform
     for (int i = tid; i < 16 * 256; i += 1024) (&wc[0][0])[i] = 0;
     __syncthreads();
-    const int a = t0 + tid;
+    const int a = c * 1024 + tid;
     const bool valid = a < A;
-    const int e = valid ? clamp_expert(p.ids[a], E) : 0;
+    const int e = ev[c];
     uint64_t peers = __ballot(valid);
     for (int bt = 0; bt < nbits; ++bt) {
       const bool bit = (e >> bt) & 1;
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(PermuteArgs p, int 
       p.s2a[pos] = a;
       p.a2s[a] = pos;
       if (p.row_token) p.row_token[pos] = a / p.k;
-      if (p.row_weight) p.row_weight[pos] = p.weights[a];
+      if (p.row_weight) p.row_weight[pos] = wv[c];
     }
     __syncthreads();
     if (tid < E) {
