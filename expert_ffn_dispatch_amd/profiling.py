@@ -7,11 +7,10 @@
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernel,
 each scaled by bytes / counter for a plain device copy of known size run in
 the same process (the copy reads and writes `copy bytes`).  The summary
-records a hash of the kernel sources so that a reader can tell when the
-counters no longer describe the built kernels.
+records a hash of the grouped expert kernels' sources so that a reader can
+tell when the counters no longer describe the built kernels.
 """
 import csv
-import glob
 import hashlib
 import os
 import statistics
@@ -20,11 +19,15 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+# sources of the grouped expert kernels, whose launch the traffic figures describe
+FFN_SOURCES = ("ffn.hip", "ffn_common.h", "common.h", "kernels.h")
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    for name in FFN_SOURCES:
+        with open(os.path.join(PKG, "csrc", name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
