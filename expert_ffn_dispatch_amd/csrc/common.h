@@ -5,6 +5,10 @@
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// 16 bytes as a native vector: loads and stores of it stay typed, so arrays
+// of them are kept in registers (a struct copy such as uint4's becomes a
+// memcpy that can pin an array to scratch memory)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace moe {
 

@@ -19,10 +19,10 @@
 //    waves.  Weights are read once per pass; the kernel is bound by HBM
 //    bandwidth.  Blocks start their walk over the contraction at different
 //    chunks so that concurrent loads spread over DRAM channels.
-//  * tile (large groups): 256-row x 256-column tiles, both operands staged
-//    through LDS (register double buffering, 16-byte chunks XOR-swizzled by
-//    row so MFMA fragment reads are free of bank conflicts), four waves of
-//    128 x 128.  Tiles are ordered row-tile-fastest and dealt to the eight
+//  * tile (large groups): 256-row x 256-column tiles, both operands loaded
+//    straight into LDS in 64-wide stages (16-byte chunks XOR-swizzled by row
+//    so MFMA fragment reads are free of bank conflicts), eight waves of
+//    128 x 64.  Tiles are ordered row-tile-fastest and dealt to the eight
 //    XCDs in contiguous runs so that tiles sharing weights or rows share an
 //    L2.
 // Both walk a tile list built in LDS from the device-side group offsets, so
@@ -368,34 +368,55 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
 //
 // 256 rows x 256 weight rows per tile (gate+up: 128 gate and the same 128 up
 // rows, i.e. 128 h columns; down: 256 output columns), eight waves in a 2 x 4
-// grid, each 128 rows x 64 weight rows, bf16 MFMA 32x32x16 (fp32 accumulate;
-// on gfx950 this shape sustains close to peak from few waves).  The k loop
-// walks 32-wide stages: every thread loads its four 16-byte chunks of stage
-// kt+3 into registers while stage kt is multiplied from LDS, and writes stage
-// kt+1 into the free LDS buffer (two LDS buffers, one barrier per stage).
-// Each LDS row is 64 B (4 chunks of 16 B); chunk c of row r lives at
-// c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which makes the 32-row fragment
-// reads conflict-free for both 32- and 64-bank LDS.  (Loading straight into
-// LDS would save the staging registers, but the compiler then waits for every
-// such load in flight before any LDS read, which serialises the ring.)
+// grid, each 128 rows x 64 weight rows, bf16 MFMA 32x32x16 (fp32 accumulate).
+// The k loop walks 64-wide stages (128 contiguous bytes of every row, one L2
+// line) through two LDS stage buffers of 64 KB: stage kt+1 is loaded while
+// stage kt is multiplied.  Stages are loaded straight into LDS (16 bytes per
+// lane, no staging registers).  Each buffer is its own LDS array and the
+// loop is unrolled over the two, so the compiler can tell which buffer a load
+// writes and does not wait for it before reading the other; each wave waits
+// for its own loads of a stage before the barrier that publishes the stage to
+// the other waves.  A direct LDS load writes 16 bytes per lane at consecutive
+// addresses, so the row swizzle is applied on the source side: the lane that
+// fills slot p of row r fetches chunk p ^ g(r), g(r) = ((r >> 1) ^ ((r & 1)
+// << 2)) & 7, which makes the 32-row fragment reads conflict-free for 32- and
+// 64-bank LDS.  Tiles are ordered row-tile-fastest and dealt to the eight XCDs
+// in contiguous runs, so tiles sharing weights or token rows share an L2.
+//
+// Measured on 16 experts x 2048 rows (M=4096, H=1536): ~1.0 PFLOP/s gate+up,
+// ~0.8 down; the same loop without its loads reaches 1.6 / 1.1 and the loads
+// alone take 75% of the full time, so the operand feed from L2 bounds it.
+// (Four waves of 128 x 128, register-staged 32-wide stages and a four-deep
+// ring of 32-wide stages all measured equal or slower.)
 
-constexpr int kTBK = 32;      // k per stage
-constexpr int kTM = 256;      // rows per tile
-constexpr int kTN = 256;      // weight rows per tile
-constexpr int kTStage = (kTM + kTN) * kTBK;   // bf16 elements per stage (32 KB)
+constexpr int kTBK = 64;                        // k per stage: 128-byte row segments
+constexpr int kTM = 256;                        // rows per tile
+constexpr int kTN = 256;                        // weight rows per tile
+constexpr int kTStage = (kTM + kTN) * kTBK;     // bf16 elements per stage (64 KB)
+constexpr int kTStageA = kTM * kTBK;            // bf16 elements of the token-row part
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int tsw(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 8 chunks of 16 B per row: chunk c of row r lives at slot c ^ g(r)
+__device__ __forceinline__ int tsw(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
+
+// s_waitcnt for vector-memory count N only (expcnt and lgkmcnt left at their maxima)
+#define MOE_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | 0x0F70)
+// s_waitcnt lgkmcnt(0) only: the fragments of a stage are known complete at
+// the end of its step
+#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
 
 template <bool GATEUP>
 __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
-  __shared__ __align__(16) uint16_t sbuf[2][kTStage];
+  __shared__ __align__(16) uint16_t sr0[kTStage];
+  __shared__ __align__(16) uint16_t sr1[kTStage];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tp[kMaxGroups + 1];
 
@@ -409,32 +430,20 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int fr = lane & 31, fg = lane >> 5;
 
-  // LDS offsets of this lane's fragments for k step s in {0, 1}: row -> the
-  // swizzled slot of chunk 2s + fg
-  int aro[4][2], bro[2][2];
+  const int swf = tsw(fr);
+  int aoff0[4], boff0[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ra = wm * 128 + 32 * i + fr;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) aro[i][s] = ra * kTBK + (((2 * s + fg) ^ tsw(ra)) << 3);
+  for (int s = 0; s < 4; ++s) {
+    aoff0[s] = (wm * 128 + fr) * kTBK + (((2 * s + fg) ^ swf) << 3);
+    boff0[s] = kTStageA + fr * kTBK + (((2 * s + fg) ^ swf) << 3);
   }
+  int brow0[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    // gate+up: block 0 = gate rows of this wave's 32 h columns, block 1 = the up rows
-    const int cb = GATEUP ? (j == 0 ? wn * 32 : HC + wn * 32) : wn * 64 + 32 * j;
-    const int rb = kTM + cb + fr;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) bro[j][s] = rb * kTBK + (((2 * s + fg) ^ tsw(rb)) << 3);
-  }
-  // this thread's four 16-byte chunks per stage: tile row tid/4 + 128*i
-  // (i = 0, 1: token rows; i = 2, 3: weight rows), chunk tid & 3
-  const int lch = tid & 3;
-  int ldst[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 2) + 128 * i;
-    ldst[i] = r * kTBK + ((lch ^ tsw(r)) << 3);
-  }
+  for (int j = 0; j < 2; ++j) brow0[j] = GATEUP ? (j == 0 ? wn * 32 : HC + wn * 32) : wn * 64 + 32 * j;
+
+  // direct LDS loads: instruction i of this wave fills rows 32*wave + 8*i +
+  // (lane >> 3) of the token part (and of the weight part), slot lane & 7
+  const int lrow = lane >> 3, lslot = lane & 7;
 
   for (int round = 0; round * G < total; ++round) {
     const int tile = round * G + slot;
@@ -447,24 +456,33 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     const int row0 = s_off[e] + rt * kTM;
     const int nrows = min(kTM, cnt - rt * kTM);
     const int col0 = ct * HC;
+    const uint16_t* wexp0 = p.w0 + (size_t)e * ncols * K;
+    const uint16_t* wexp1 = GATEUP ? p.w1 + (size_t)e * ncols * K : wexp0;
 
-    // the four source rows (scalars, not an array, so they stay in registers)
-    const uint16_t *src0, *src1, *src2, *src3;
-    {
-      const int r0 = tid >> 2, r1 = r0 + 128;
-      const int g0 = p.a_rows ? p.a_rows[row0 + (r0 < nrows ? r0 : 0)] : row0 + (r0 < nrows ? r0 : 0);
-      const int g1 = p.a_rows ? p.a_rows[row0 + (r1 < nrows ? r1 : 0)] : row0 + (r1 < nrows ? r1 : 0);
-      src0 = p.a + (size_t)g0 * K + lch * 8;
-      src1 = p.a + (size_t)g1 * K + lch * 8;
-      // weight rows r0 and r1 of the tile (gate+up: r1 >= 128 is an up row)
-      const bool up0 = GATEUP && r0 >= HC, up1 = GATEUP && r1 >= HC;
-      int wc0 = col0 + (up0 ? r0 - HC : r0), wc1 = col0 + (up1 ? r1 - HC : r1);
-      if (wc0 >= ncols) wc0 = col0;               // partial column tile
-      if (wc1 >= ncols) wc1 = col0;
-      src2 = (up0 ? p.w1 : p.w0) + ((size_t)e * ncols + wc0) * K + lch * 8;
-      src3 = (up1 ? p.w1 : p.w0) + ((size_t)e * ncols + wc1) * K + lch * 8;
+    const uint16_t* asrc[4];
+    const uint16_t* bsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * wave + 8 * i + lrow;
+      const int ch = lslot ^ tsw(r);
+      const int rr = (r < nrows) ? r : 0;
+      const int grow = p.a_rows ? p.a_rows[row0 + rr] : (row0 + rr);
+      asrc[i] = p.a + (size_t)grow * K + ch * 8;
+      int wc = col0 + ((GATEUP && r >= HC) ? r - HC : r);
+      if (wc >= ncols) wc = col0;                // partial column tile: any valid row
+      bsrc[i] = ((GATEUP && r >= HC) ? wexp1 : wexp0) + (size_t)wc * K + ch * 8;
     }
-#define MOE_LD(PTR, KO) (*reinterpret_cast<const uint4*>((PTR) + (KO)))
+    const int ldsA = (32 * wave) * kTBK;
+    const int ldsB = kTStageA + (32 * wave) * kTBK;
+
+#define MOE_DMA(BUF, KT_)                                                                          \
+  {                                                                                                \
+    const int ko_ = ((KT_) < KT ? (KT_) : KT - 1) * kTBK;                                         \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                \
+      __builtin_amdgcn_global_load_lds(asrc[i] + ko_, (BUF) + ldsA + 8 * i * kTBK, 16, 0, 0);     \
+      __builtin_amdgcn_global_load_lds(bsrc[i] + ko_, (BUF) + ldsB + 8 * i * kTBK, 16, 0, 0);     \
+    }                                                                                              \
+  }
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -474,53 +492,50 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    // prologue: stage 0 into LDS buffer 0, stages 1 and 2 into registers
-    __syncthreads();   // LDS free (previous tile done)
-    *reinterpret_cast<uint4*>(&sbuf[0][ldst[0]]) = MOE_LD(src0, 0);
-    *reinterpret_cast<uint4*>(&sbuf[0][ldst[1]]) = MOE_LD(src1, 0);
-    *reinterpret_cast<uint4*>(&sbuf[0][ldst[2]]) = MOE_LD(src2, 0);
-    *reinterpret_cast<uint4*>(&sbuf[0][ldst[3]]) = MOE_LD(src3, 0);
-    const int k1 = (KT > 1 ? 1 : 0) * kTBK, k2 = (KT > 2 ? 2 : 0) * kTBK;
-    // two register sets take turns (no copies, which would force a wait on
-    // the newer loads): at stage kt the set holding stage kt+1 is written to
-    // LDS and refilled with stage kt+3
-    uint4 x0 = MOE_LD(src0, k1), x1 = MOE_LD(src1, k1), x2 = MOE_LD(src2, k1), x3 = MOE_LD(src3, k1);
-    uint4 y0 = MOE_LD(src0, k2), y1 = MOE_LD(src1, k2), y2 = MOE_LD(src2, k2), y3 = MOE_LD(src3, k2);
+    // the previous tile's last reads of the buffers are done
+    __syncthreads();
+    MOE_DMA(sr0, 0)
 
-#define MOE_KSTEP(KT_, R0, R1, R2, R3)                                                            \
-    do {                                                                                          \
-      __syncthreads();   /* stage KT_ visible; every wave is done with stage KT_-1 */             \
-      /* stage KT_+1 -> the other buffer (read last at stage KT_-1); the last */                  \
-      /* stages re-write valid data so stores stay unconditional */                               \
-      uint16_t* Ln_ = sbuf[((KT_) + 1) & 1];                                                      \
-      *reinterpret_cast<uint4*>(&Ln_[ldst[0]]) = R0;                                              \
-      *reinterpret_cast<uint4*>(&Ln_[ldst[1]]) = R1;                                              \
-      *reinterpret_cast<uint4*>(&Ln_[ldst[2]]) = R2;                                              \
-      *reinterpret_cast<uint4*>(&Ln_[ldst[3]]) = R3;                                              \
-      const int k3_ = ((KT_) + 3 < KT ? (KT_) + 3 : KT - 1) * kTBK;                               \
-      R0 = MOE_LD(src0, k3_); R1 = MOE_LD(src1, k3_); R2 = MOE_LD(src2, k3_); R3 = MOE_LD(src3, k3_); \
-      const uint16_t* L_ = sbuf[(KT_) & 1];                                                       \
-      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                          \
-        uint4 af[4], bf[2];                                                                       \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(L_ + aro[i][ks]); \
-        _Pragma("unroll") for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const uint4*>(L_ + bro[j][ks]); \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                             \
+    // one stage: wait for this wave's loads of stage KT_, publish it with the
+    // barrier, start stage KT_+1 into the other buffer (every wave finished
+    // reading it before the barrier), multiply stage KT_
+#define MOE_TSTEP(BUF, NBUF, KT_)                                                                  \
+  {                                                                                                \
+    MOE_WAIT_VM(0);                                                                                \
+    __builtin_amdgcn_s_barrier();                                                                  \
+    MOE_DMA(NBUF, (KT_) + 1)                                                                       \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                                \
+      u32x4_t af[4], bf[2];                                                                        \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+          af[i] = *reinterpret_cast<const u32x4_t*>((BUF) + aoff0[s] + 32 * i * kTBK);            \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
+          bf[j] = *reinterpret_cast<const u32x4_t*>((BUF) + boff0[s] + brow0[j] * kTBK);          \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
           _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]); \
-      }                                                                                           \
-    } while (0)
+    }                                                                                              \
+    MOE_WAIT_LGKM0();                                                                              \
+  }
 
-    // K % 64 == 0 (checked at the boundary), so KT is even and both steps
-    // of an iteration always run (a conditional second step would make the
-    // compiler wait for every load in flight at the loop head)
-    for (int kt = 0; kt < KT; kt += 2) {
-      MOE_KSTEP(kt, x0, x1, x2, x3);
-      MOE_KSTEP(kt + 1, y0, y1, y2, y3);
+    // the loop names each buffer explicitly (see above); an odd stage count
+    // ends with one more step on the first buffer
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      MOE_TSTEP(sr0, sr1, kt)
+      MOE_TSTEP(sr1, sr0, kt + 1)
     }
-#undef MOE_KSTEP
-#undef MOE_LD
+    if (kt < KT) MOE_TSTEP(sr0, sr1, kt)
+#undef MOE_TSTEP
+#undef MOE_DMA
+    MOE_WAIT_VM(0);
+    // down: the tile's row scales through LDS (the first buffer is free once
+    // every wave has finished its last stage)
+    float* s_scale = reinterpret_cast<float*>(sr0);
+    if (!GATEUP) {
+      __syncthreads();
+      if (tid < kTM) s_scale[tid] = (p.row_scale && tid < nrows) ? p.row_scale[row0 + tid] : 1.f;
+      __syncthreads();
+    }
 
-    // ---- epilogue: lane holds column fr of each 32 x 32 block, rows
-    // 8b + 4*fg + q for element 4b + q; 32 lanes store 64 contiguous bytes ----
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -535,7 +550,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
             const float g = acc[i][0][4 * b + q], u = acc[i][1][4 * b + q];
             if (col < ncols) orow[col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
           } else {
-            const float sc = p.row_scale ? p.row_scale[row0 + row] : 1.f;
+            const float sc = s_scale[row];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const int col = col0 + wn * 64 + 32 * j + fr;
@@ -547,6 +562,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     }
   }
 }
+#undef MOE_WAIT_VM
+#undef MOE_WAIT_LGKM0
 
 // ================================ launchers =================================
 
