@@ -9,9 +9,10 @@ SwiGLU (gate+up, down) -> shared experts -> combine.  The default workload is
 the Mixtral-8x22B-shaped decode batch (N=156 tokens, M=6144, E=8, top-2,
 H=16384), the batch the MegaScale-Infer summary uses to show 39 rows per
 expert.  Prints ONE JSON line: tokens/s over K timed back-to-back steps, the
-per-stage times from events recorded inside the layer, the roofline of the
-dominant kernel (the gate+up GEMM, HBM-bound at this batch) and the oracle
-timed on the host cores as a CPU baseline.
+per-stage times from events recorded inside the layer during K further
+(instrumented) steps, the roofline of the dominant kernel (the gate+up GEMM,
+HBM-bound at this batch) and the oracle timed on the host cores as a CPU
+baseline.
 """
 import argparse
 import json
@@ -139,13 +140,21 @@ def main() -> int:
         for e in row:
             e.record()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    # timed steps: back-to-back layer calls with nothing else on the stream
+    wall = 0.0
+    if flush_buf is None:
+        t0 = time.perf_counter()
+        for i in range(K):
+            step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    # instrumented steps (stage events inside the layer): per-stage times and,
+    # with --flush, the layer time between its first and last event
     for i in range(K):
         if flush_buf is not None:
             flush_buf.fill_(i & 0xff)
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
     stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(6)] for i in range(K)])
     layer_ms = np.array([evs[i][0].elapsed_time(evs[i][6]) for i in range(K)])
