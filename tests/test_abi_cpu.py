@@ -79,7 +79,11 @@ def test_route_pointer_checks(lib):
     assert "aligned" in _err(lib)
     assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, MIS, FAKE, FAKE, FAKE, 1 << 30, None) == _lib.MOE_ERR_INVALID
     assert lib.moe_route(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
-    assert moe.moe_route_workspace_bytes(D(N=156, M=6144, E=8)) >= 16 * 6144 * 2
+    # small batches keep fp32 partial scores per contraction slice; larger
+    # ones also hold the transposed router (E padded to 16)
+    small = moe.moe_route_workspace_bytes(D(N=156, M=6144, E=8))
+    assert small >= 156 * 8 * 4 and small % 256 == 0
+    assert moe.moe_route_workspace_bytes(D(N=4096, M=6144, E=8)) >= 16 * 6144 * 2 + 4096 * 16 * 4
 
 
 def _layer(lib, d, flags=0, ws_bytes=None, **over):
