@@ -10,8 +10,10 @@
 // Three launches, no atomics on anything that orders rows:
 //   hist    - one block per tile of 256 assignments: LDS histogram (integer
 //             atomics only count) -> tile_hist[e][t]
-//   scan    - one block: per expert, exclusive scan of tile_hist over tiles
-//             (wave shuffles) -> tile_off; then counts and offsets
+//   scan    - one block per expert: exclusive scan of tile_hist over the
+//             tiles -> tile_off, and the expert's count
+//   (the scatter blocks each scan the counts into the expert offsets; the
+//   first one also stores them)
 //   scatter - one block per tile: rank inside the tile from wave ballots
 //             (lanes with the same expert and a lower lane id) plus the
 //             counts of earlier waves, so sorted slot =
@@ -40,61 +42,80 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   if (tid < E) tile_hist[(size_t)tid * T + tile] = h[tid];
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ tile_hist, int E, int T,
-                                                    int32_t* __restrict__ tile_off,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets) {
-  __shared__ int cnt[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = wave; e < E; e += 16) {
-    int running = 0;
-    for (int t0 = 0; t0 < T; t0 += 64) {
-      const int t = t0 + lane;
-      const int v = (t < T) ? tile_hist[(size_t)e * T + t] : 0;
-      int inc = v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(inc, off);
-        if (lane >= off) inc += o;
-      }
-      if (t < T) tile_off[(size_t)e * T + t] = running + inc - v;
-      running += __shfl(inc, 63);
-    }
-    if (lane == 0) cnt[e] = running;
-  }
-  __syncthreads();
-  if (wave == 0) {
+// One block per expert: exclusive scan of its tile counts over the tiles,
+// 1024 tiles per pass (four consecutive per thread), and the expert's total.
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ tile_hist, int T,
+                                                   int32_t* __restrict__ tile_off, int32_t* __restrict__ counts) {
+  __shared__ int wsum[4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* h = tile_hist + (size_t)e * T;
+  int32_t* o = tile_off + (size_t)e * T;
+  int carry = 0;
+  for (int t0 = 0; t0 < T; t0 += 1024) {
     int v[4], s = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      v[i] = (e < E) ? cnt[e] : 0;
+      const int t = t0 + tid * 4 + i;
+      v[i] = t < T ? h[t] : 0;
       s += v[i];
     }
     int inc = s;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(inc, off);
-      if (lane >= off) inc += o;
+      const int q = __shfl_up(inc, off);
+      if (lane >= off) inc += q;
     }
-    int base = inc - s;
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    int run = before + inc - s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      if (e < E) {
-        counts[e] = v[i];
-        offsets[e] = base;
-      }
-      base += v[i];
+      const int t = t0 + tid * 4 + i;
+      if (t < T) o[t] = run;
+      run += v[i];
     }
-    if (lane == 63) offsets[E] = inc;
+    carry += total;
+    __syncthreads();              // wsum is rewritten by the next pass
   }
+  if (tid == 0) counts[e] = carry;
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(PermuteArgs p, int T, int nbits) {
   __shared__ int wc[4][256];
+  __shared__ int s_base[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, tile = blockIdx.x;
   for (int i = tid; i < 4 * 256; i += 256) (&wc[0][0])[i] = 0;
+  // expert offsets: exclusive scan of the counts (every block; block 0 also
+  // publishes them)
+  if (wave == 0) {
+    int v[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      v[i] = (e < p.E) ? p.counts[e] : 0;
+      s += v[i];
+    }
+    int inc = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int q = __shfl_up(inc, off);
+      if (lane >= off) inc += q;
+    }
+    int b = inc - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane * 4 + i;
+      if (e < p.E) {
+        s_base[e] = b;
+        if (tile == 0) p.offsets[e] = b;
+      }
+      b += v[i];
+    }
+    if (tile == 0 && lane == 63) p.offsets[p.E] = inc;
+  }
   __syncthreads();
   const int a = tile * kPermTile + tid;
   const bool valid = a < p.A;
@@ -111,7 +132,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(PermuteArgs p, int T, int 
   if (valid) {
     int before = 0;
     for (int w = 0; w < wave; ++w) before += wc[w][e];
-    const int pos = p.offsets[e] + p.tile_off[(size_t)e * T + tile] + before + rank;
+    const int pos = s_base[e] + p.tile_off[(size_t)e * T + tile] + before + rank;
     p.s2a[pos] = a;
     p.a2s[a] = pos;
     if (p.row_token) p.row_token[pos] = a / p.k;
@@ -244,8 +265,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   if (T > 0) {
     hipLaunchKernelGGL(hist_kernel, dim3(T), dim3(256), 0, st, a.ids, a.A, a.E, T, a.tile_hist);
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, a.tile_hist, a.E, T, a.tile_off,
-                     a.counts, a.offsets);
+  hipLaunchKernelGGL(scan_kernel, dim3(a.E), dim3(256), 0, st, a.tile_hist, T, a.tile_off, a.counts);
   if (T > 0) {
     hipLaunchKernelGGL(scatter_kernel, dim3(T), dim3(256), 0, st, a, T, nbits);
   }

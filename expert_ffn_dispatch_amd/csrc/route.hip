@@ -14,9 +14,10 @@
 // top-k.  Other batches take three:
 //   transpose - W_r [M][E] -> W_rT [EP][M] (E padded to 16), so that both MFMA
 //               operands read 16 contiguous bytes of the contraction per lane
-//   logits    - one wave per (16-64 tokens, k slice): partial scores for all
-//               experts; the contraction is split into KS slices so that even
-//               a decode batch spreads over hundreds of waves
+//   logits    - one block per (16-64 tokens, up to 80 experts, k slice),
+//               its four waves splitting the slice: partial scores per slice;
+//               the contraction is split into KS slices so that even a
+//               decode batch spreads over many waves
 //   topk      - one wave per token: sums the KS partials in slice order
 //               (deterministic), adds the bias, wave-wide arg-max k times
 //               (ties to the lower id), renormalises.
@@ -55,53 +56,79 @@ __global__ __launch_bounds__(256) void router_transpose_kernel(const uint16_t* _
   }
 }
 
-// part[ks][n][e] = sum over the slice's k of x[n,k] * W_r[k,e].  One wave
-// covers RW x 16 tokens and all experts for one k slice, so each router
-// fragment it loads serves RW token blocks.
-template <int NCB, int RW>
+// part[ks][n][e] = sum over the slice's k of x[n,k] * W_r[k,e].  A block
+// covers RW x 16 tokens (blockIdx.x) and NCBW x 16 experts (expert group
+// blockIdx.z) for one k slice (blockIdx.y); its four waves take consecutive
+// quarters of the slice, and their partial tiles are added in wave order
+// through LDS, so the slice's partials leave the block once.  Each router
+// fragment a wave loads serves RW token blocks and each token fragment NCBW
+// expert blocks; the next 32-wide step is loaded while the current one is
+// multiplied (two register sets).
+template <int NCBW, int RW>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ wt, int N, int M,
+                                                            const uint16_t* __restrict__ wt, int N, int M, int EP,
                                                             int steps_per_slice, float* __restrict__ part) {
-  constexpr int EP = NCB * 16;
+  constexpr int NV = RW * NCBW * 4;             // accumulator values per lane
+  __shared__ float red[4][NV][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tg = blockIdx.x * 4 + wave;
-  const int tok0 = tg * 16 * RW;
-  if (tok0 >= N) return;
+  const int tok0 = blockIdx.x * 16 * RW;
   const int ks = blockIdx.y;
-  const int s0 = ks * steps_per_slice;
-  const int s1 = min(M / 32, s0 + steps_per_slice);
+  const int eb0 = blockIdx.z * NCBW;             // first 16-expert block
+  const int b0 = ks * steps_per_slice;
+  const int b1 = min(M / 32, b0 + steps_per_slice);
+  const int s0 = b0 + ((b1 - b0) * wave) / 4, s1 = b0 + ((b1 - b0) * (wave + 1)) / 4;
   const int r = lane & 15, g = lane >> 4;
   const uint16_t* xa[RW];
 #pragma unroll
   for (int t = 0; t < RW; ++t) xa[t] = x + (size_t)min(tok0 + 16 * t + r, N - 1) * M + g * 8;
-  const uint16_t* wb = wt + (size_t)r * M + g * 8;
+  const uint16_t* wb = wt + (size_t)(eb0 * 16 + r) * M + g * 8;
 
-  f32x4_t acc[RW][NCB];
+  f32x4_t acc[RW][NCBW];
 #pragma unroll
   for (int t = 0; t < RW; ++t)
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s = s0; s < s1; ++s) {
-    uint4 a[RW], b[NCB];
-#pragma unroll
-    for (int t = 0; t < RW; ++t) a[t] = *reinterpret_cast<const uint4*>(xa[t] + s * 32);
-#pragma unroll
-    for (int c = 0; c < NCB; ++c) b[c] = *reinterpret_cast<const uint4*>(wb + (size_t)c * 16 * M + s * 32);
-#pragma unroll
-    for (int t = 0; t < RW; ++t)
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) acc[t][c] = mfma16(a[t], b[c], acc[t][c]);
+    for (int c = 0; c < NCBW; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t pa[RW], pb[NCBW], qa[RW], qb[NCBW];
+#define MOE_RLOAD(A_, B_, S_)                                                                       \
+  {                                                                                                 \
+    _Pragma("unroll") for (int t = 0; t < RW; ++t)                                                  \
+        A_[t] = *reinterpret_cast<const u32x4_t*>(xa[t] + (S_) * 32);                               \
+    _Pragma("unroll") for (int c = 0; c < NCBW; ++c)                                                \
+        B_[c] = *reinterpret_cast<const u32x4_t*>(wb + (size_t)c * 16 * M + (S_) * 32);             \
   }
-  float* out = part + (size_t)ks * N * EP;
+#define MOE_RMMA(A_, B_)                                                                            \
+  _Pragma("unroll") for (int t = 0; t < RW; ++t)                                                    \
+      _Pragma("unroll") for (int c = 0; c < NCBW; ++c) acc[t][c] = mfma16(A_[t], B_[c], acc[t][c]);
+  if (s0 < s1) {
+    MOE_RLOAD(pa, pb, s0)
+    int st = s0;
+    for (; st + 1 < s1; st += 2) {
+      MOE_RLOAD(qa, qb, st + 1)
+      MOE_RMMA(pa, pb)
+      MOE_RLOAD(pa, pb, min(st + 2, s1 - 1))   // the last step re-reads itself
+      MOE_RMMA(qa, qb)
+    }
+    if (st < s1) { MOE_RMMA(pa, pb) }
+  }
+#undef MOE_RLOAD
+#undef MOE_RMMA
 #pragma unroll
   for (int t = 0; t < RW; ++t)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = tok0 + 16 * t + g * 4 + q;
-      if (n >= N) continue;
+    for (int c = 0; c < NCBW; ++c)
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) out[(size_t)n * EP + c * 16 + r] = acc[t][c][q];
-    }
+      for (int q = 0; q < 4; ++q) red[wave][(t * NCBW + c) * 4 + q][lane] = acc[t][c][q];
+  __syncthreads();
+  // value v of lane l: token tok0 + 16t + 4(l >> 4) + q, expert (eb0 + c)*16 + (l & 15)
+  float* out = part + (size_t)ks * N * EP;
+  for (int i = threadIdx.x; i < NV * 64; i += 256) {
+    const int v = i >> 6, l = i & 63;
+    const int q = v & 3, c = (v >> 2) % NCBW, t = (v >> 2) / NCBW;
+    const int n = tok0 + 16 * t + 4 * (l >> 4) + q;
+    if (n >= N) continue;
+    const float s = red[0][v][l] + red[1][v][l] + red[2][v][l] + red[3][v][l];
+    out[(size_t)n * EP + (eb0 + c) * 16 + (l & 15)] = s;
+  }
 }
 
 template <int PER>
@@ -260,7 +287,7 @@ void small_route_plan(int N, int M, int& slice, int& KS) {
 }
 
 struct RoutePlan {
-  int NCB, EP, RW, KS, steps;
+  int NCB, EP, NCBW, EG, RW, KS, steps;
 };
 
 RoutePlan plan(int N, int M, int E) {
@@ -268,13 +295,17 @@ RoutePlan plan(int N, int M, int E) {
   const int ncb = ceil_div(E, 16);
   p.NCB = ncb <= 1 ? 1 : ncb <= 2 ? 2 : ncb <= 4 ? 4 : ncb <= 8 ? 8 : ncb <= 10 ? 10 : ncb <= 12 ? 12 : 16;
   p.EP = p.NCB * 16;
+  // expert blocks per wave: at most five, so that two register sets of
+  // operands and the accumulators fit; the rest go to more blocks
+  p.NCBW = p.NCB <= 4 ? p.NCB : p.NCB == 10 ? 5 : 4;
+  p.EG = p.NCB / p.NCBW;
   // tokens per wave: more rows reuse each router fragment, fewer rows spread
   // a small batch over more waves
-  p.RW = (N >= 2048 && p.NCB <= 8) ? 4 : (N >= 512 ? 2 : 1);
-  const int waves = ceil_div(N, 16 * p.RW);
+  p.RW = N >= 2048 ? 4 : (N >= 512 ? 2 : 1);
+  const int blocks = ceil_div(N, 16 * p.RW) * p.EG;
   const int total_steps = M / 32;
-  int ks = ceil_div(2048, waves);
-  const int max_ks = ceil_div(total_steps, 4);      // slices of at least 128 k
+  int ks = ceil_div(1024, blocks);
+  const int max_ks = ceil_div(total_steps, 16);     // slices of at least 512 k (128 per wave)
   if (ks > max_ks) ks = max_ks;
   // partial scores are written and re-read once: keep them small
   while (ks > 1 && (size_t)ks * N * p.EP * 4 > ((size_t)16 << 20)) --ks;
@@ -284,17 +315,17 @@ RoutePlan plan(int N, int M, int E) {
   return p;
 }
 
-template <int NCB, int RW>
+template <int NCBW, int RW>
 void launch_logits_rw(const RouteArgs& a, const RoutePlan& pl, const uint16_t* wt, float* part, hipStream_t st) {
-  hipLaunchKernelGGL((router_logits_kernel<NCB, RW>), dim3(ceil_div(a.N, 64 * RW), pl.KS), dim3(256), 0, st, a.x,
-                     wt, a.N, a.M, pl.steps, part);
+  hipLaunchKernelGGL((router_logits_kernel<NCBW, RW>), dim3(ceil_div(a.N, 16 * RW), pl.KS, pl.EG), dim3(256), 0,
+                     st, a.x, wt, a.N, a.M, pl.EP, pl.steps, part);
 }
 
-template <int NCB>
+template <int NCBW>
 void launch_logits(const RouteArgs& a, const RoutePlan& pl, const uint16_t* wt, float* part, hipStream_t st) {
-  if (pl.RW == 4) launch_logits_rw<NCB, (NCB <= 8 ? 4 : 2)>(a, pl, wt, part, st);
-  else if (pl.RW == 2) launch_logits_rw<NCB, 2>(a, pl, wt, part, st);
-  else launch_logits_rw<NCB, 1>(a, pl, wt, part, st);
+  if (pl.RW == 4) launch_logits_rw<NCBW, 4>(a, pl, wt, part, st);
+  else if (pl.RW == 2) launch_logits_rw<NCBW, 2>(a, pl, wt, part, st);
+  else launch_logits_rw<NCBW, 1>(a, pl, wt, part, st);
 }
 
 }  // namespace
@@ -340,14 +371,11 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + (((size_t)pl.EP * a.M * 2 + 255) & ~size_t(255)));
   hipLaunchKernelGGL(router_transpose_kernel, dim3(a.M / 64, ceil_div(pl.EP, 64)), dim3(256), 0, st, a.w_router,
                      a.M, a.E, pl.EP, wt);
-  switch (pl.NCB) {
+  switch (pl.NCBW) {
     case 1: launch_logits<1>(a, pl, wt, part, st); break;
     case 2: launch_logits<2>(a, pl, wt, part, st); break;
-    case 4: launch_logits<4>(a, pl, wt, part, st); break;
-    case 8: launch_logits<8>(a, pl, wt, part, st); break;
-    case 10: launch_logits<10>(a, pl, wt, part, st); break;
-    case 12: launch_logits<12>(a, pl, wt, part, st); break;
-    default: launch_logits<16>(a, pl, wt, part, st); break;
+    case 5: launch_logits<5>(a, pl, wt, part, st); break;
+    default: launch_logits<4>(a, pl, wt, part, st); break;
   }
   const int per = ceil_div(pl.EP, 64);
   const dim3 g(ceil_div(a.N, 4));
