@@ -390,10 +390,7 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
 // ring of 32-wide stages all measured equal or slower.)
 
 constexpr int kTBK = 64;                        // k per stage: 128-byte row segments
-constexpr int kTM = 256;                        // rows per tile
 constexpr int kTN = 256;                        // weight rows per tile
-constexpr int kTStage = (kTM + kTN) * kTBK;     // bf16 elements per stage (64 KB)
-constexpr int kTStageA = kTM * kTBK;            // bf16 elements of the token-row part
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -405,6 +402,13 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
 // 8 chunks of 16 B per row: chunk c of row r lives at slot c ^ g(r)
 __device__ __forceinline__ int tsw(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
 
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// lds + 16 l (the LDS address must be the same in every lane).  A plain
+// function, so that kernel templates call no target builtin directly.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
 // s_waitcnt for vector-memory count N only (expcnt and lgkmcnt left at their maxima)
 #define MOE_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | 0x0F70)
 // s_waitcnt lgkmcnt(0) only: the fragments of a stage are known complete at
@@ -412,11 +416,16 @@ __device__ __forceinline__ int tsw(int row) { return ((row >> 1) ^ ((row & 1) <<
 #define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 
-template <bool GATEUP>
+// BM token rows per tile (256, 192 or 128): each wave covers BM/2 rows,
+// FMW = BM/64 blocks of 32.
+template <bool GATEUP, int BM>
 __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
-  __shared__ __align__(16) uint16_t sr0[kTStage];
-  __shared__ __align__(16) uint16_t sr1[kTStage];
+  constexpr int FMW = BM / 64;                   // 32-row MFMA blocks per wave
+  constexpr int AI = BM / 64;                    // direct loads of token rows per wave per stage
+  constexpr int STA = BM * kTBK;                 // bf16 elements of the token-row part
+  __shared__ __align__(16) uint16_t sr0[(BM + kTN) * kTBK];
+  __shared__ __align__(16) uint16_t sr1[(BM + kTN) * kTBK];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tp[kMaxGroups + 1];
 
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
   const int K = p.K, ncols = p.ncols;
   const int NT = ceil_div(ncols, HC);            // the last column tile may be partial
   const int KT = K / kTBK;
-  const int total = build_tile_list<kTM>(p, NT, s_off, s_tp);
+  const int total = build_tile_list<BM>(p, NT, s_off, s_tp);
   const int G = gridDim.x;                       // a multiple of 8
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int fr = lane & 31, fg = lane >> 5;
@@ -434,15 +443,16 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
   int aoff0[4], boff0[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    aoff0[s] = (wm * 128 + fr) * kTBK + (((2 * s + fg) ^ swf) << 3);
-    boff0[s] = kTStageA + fr * kTBK + (((2 * s + fg) ^ swf) << 3);
+    aoff0[s] = (wm * (BM / 2) + fr) * kTBK + (((2 * s + fg) ^ swf) << 3);
+    boff0[s] = STA + fr * kTBK + (((2 * s + fg) ^ swf) << 3);
   }
   int brow0[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) brow0[j] = GATEUP ? (j == 0 ? wn * 32 : HC + wn * 32) : wn * 64 + 32 * j;
 
-  // direct LDS loads: instruction i of this wave fills rows 32*wave + 8*i +
-  // (lane >> 3) of the token part (and of the weight part), slot lane & 7
+  // direct LDS loads: instruction i of this wave fills token rows
+  // (BM/8)*wave + 8*i + (lane >> 3) and weight rows 32*wave + 8*i + (lane >> 3),
+  // slot lane & 7
   const int lrow = lane >> 3, lslot = lane & 7;
 
   for (int round = 0; round * G < total; ++round) {
@@ -450,43 +460,48 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     if (tile >= total) continue;
     const int e = find_group(s_tp, p.E, tile);
     const int cnt = s_off[e + 1] - s_off[e];
-    const int RT = ceil_div(cnt, kTM);
+    const int RT = ceil_div(cnt, BM);
     const int local = tile - s_tp[e];
     const int ct = local / RT, rt = local - ct * RT;
-    const int row0 = s_off[e] + rt * kTM;
-    const int nrows = min(kTM, cnt - rt * kTM);
+    const int row0 = s_off[e] + rt * BM;
+    const int nrows = min(BM, cnt - rt * BM);
     const int col0 = ct * HC;
     const uint16_t* wexp0 = p.w0 + (size_t)e * ncols * K;
     const uint16_t* wexp1 = GATEUP ? p.w1 + (size_t)e * ncols * K : wexp0;
 
-    const uint16_t* asrc[4];
+    const uint16_t* asrc[AI];
     const uint16_t* bsrc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 32 * wave + 8 * i + lrow;
+    for (int i = 0; i < AI; ++i) {
+      const int r = (BM / 8) * wave + 8 * i + lrow;
       const int ch = lslot ^ tsw(r);
       const int rr = (r < nrows) ? r : 0;
       const int grow = p.a_rows ? p.a_rows[row0 + rr] : (row0 + rr);
       asrc[i] = p.a + (size_t)grow * K + ch * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * wave + 8 * i + lrow;
+      const int ch = lslot ^ tsw(r);
       int wc = col0 + ((GATEUP && r >= HC) ? r - HC : r);
       if (wc >= ncols) wc = col0;                // partial column tile: any valid row
       bsrc[i] = ((GATEUP && r >= HC) ? wexp1 : wexp0) + (size_t)wc * K + ch * 8;
     }
-    const int ldsA = (32 * wave) * kTBK;
-    const int ldsB = kTStageA + (32 * wave) * kTBK;
+    const int ldsA = ((BM / 8) * wave) * kTBK;
+    const int ldsB = STA + (32 * wave) * kTBK;
 
 #define MOE_DMA(BUF, KT_)                                                                          \
   {                                                                                                \
     const int ko_ = ((KT_) < KT ? (KT_) : KT - 1) * kTBK;                                         \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                \
-      __builtin_amdgcn_global_load_lds(asrc[i] + ko_, (BUF) + ldsA + 8 * i * kTBK, 16, 0, 0);     \
-      __builtin_amdgcn_global_load_lds(bsrc[i] + ko_, (BUF) + ldsB + 8 * i * kTBK, 16, 0, 0);     \
-    }                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                 \
+        dma16(asrc[i] + ko_, (BUF) + ldsA + 8 * i * kTBK);                                         \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
+        dma16(bsrc[i] + ko_, (BUF) + ldsB + 8 * i * kTBK);                                         \
   }
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[FMW][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FMW; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -505,12 +520,12 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     __builtin_amdgcn_s_barrier();                                                                  \
     MOE_DMA(NBUF, (KT_) + 1)                                                                       \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                                \
-      u32x4_t af[4], bf[2];                                                                        \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+      u32x4_t af[FMW], bf[2];                                                                      \
+      _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
           af[i] = *reinterpret_cast<const u32x4_t*>((BUF) + aoff0[s] + 32 * i * kTBK);            \
       _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
           bf[j] = *reinterpret_cast<const u32x4_t*>((BUF) + boff0[s] + brow0[j] * kTBK);          \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+      _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
           _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]); \
     }                                                                                              \
     MOE_WAIT_LGKM0();                                                                              \
@@ -532,17 +547,17 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     float* s_scale = reinterpret_cast<float*>(sr0);
     if (!GATEUP) {
       __syncthreads();
-      if (tid < kTM) s_scale[tid] = (p.row_scale && tid < nrows) ? p.row_scale[row0 + tid] : 1.f;
+      if (tid < BM) s_scale[tid] = (p.row_scale && tid < nrows) ? p.row_scale[row0 + tid] : 1.f;
       __syncthreads();
     }
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FMW; ++i) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int row = wm * 128 + 32 * i + 8 * b + 4 * fg + q;
+          const int row = wm * (BM / 2) + 32 * i + 8 * b + 4 * fg + q;
           if (row >= nrows) continue;
           uint16_t* orow = p.out + (size_t)(row0 + row) * ncols;
           if (GATEUP) {
@@ -579,17 +594,28 @@ hipError_t launch_stream(const FfnArgs& a, int num_cu, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool GATEUP>
-hipError_t launch_tile(const FfnArgs& a, int num_cu, hipStream_t st) {
+template <bool GATEUP, int BM>
+hipError_t launch_tile_bm(const FfnArgs& a, int num_cu, hipStream_t st) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;
   const int NT = ceil_div(a.ncols, HC);
-  const long ub_rows = a.rows_total / kTM + (a.E < a.rows_total ? a.E : a.rows_total);
+  const long ub_rows = a.rows_total / BM + (a.E < a.rows_total ? a.E : a.rows_total);
   const long ub = ub_rows * NT;
   long grid = (num_cu / 8) * 8;
   if (ub < grid) grid = ((ub + 7) / 8) * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM>), dim3((unsigned)grid), dim3(512), 0, st, a);
   return hipGetLastError();
+}
+
+// Tile height from the mean rows per group: the smallest of 128 / 192 / 256
+// that holds 1.25x the mean, so that typical groups fill one row tile (a
+// 256-row tile over 154-row groups wastes 40% of its MFMA work).
+template <bool GATEUP>
+hipError_t launch_tile(const FfnArgs& a, int num_cu, hipStream_t st) {
+  const double need = 1.25 * (double)a.rows_total / (a.E > 0 ? a.E : 1);
+  if (need <= 128.0) return launch_tile_bm<GATEUP, 128>(a, num_cu, st);
+  if (need <= 192.0) return launch_tile_bm<GATEUP, 192>(a, num_cu, st);
+  return launch_tile_bm<GATEUP, 256>(a, num_cu, st);
 }
 
 // The split-contraction decode kernel pays off only when the plain streaming
