@@ -389,12 +389,19 @@ int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe
   moe::FfnArgs g{x, w.row_token, w.offsets, 0, w_gate, w_up, nullptr, w.h, E, A, M, H};
   if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
   if (hipError_t e = mark(4)) return device_error(fn, e);
-  moe::FfnArgs dn{w.h, nullptr, w.offsets, 0, w_down, nullptr, w.row_weight, w.y, E, A, H, M};
+  // top-1 routing without shared experts: every token has exactly one row,
+  // so the down GEMM stores it straight into the output (the combine would
+  // only copy it)
+  const bool direct = (k == 1 && dims->n_shared == 0);
+  moe::FfnArgs dn{w.h, nullptr, w.offsets, 0, w_down, nullptr, w.row_weight, direct ? out : w.y, E, A, H, M,
+                  direct ? w.row_token : nullptr};
   if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
   if (hipError_t e = mark(5)) return device_error(fn, e);
 
-  moe::CombineArgs cb{w.y, w.a2s, nullptr, w.ys, out, N, M, k};
-  if (hipError_t e = moe::launch_combine(cb, st)) return device_error(fn, e);
+  if (!direct) {
+    moe::CombineArgs cb{w.y, w.a2s, nullptr, w.ys, out, N, M, k};
+    if (hipError_t e = moe::launch_combine(cb, st)) return device_error(fn, e);
+  }
   if (hipError_t e = mark(6)) return device_error(fn, e);
   return ok();
 }

@@ -205,8 +205,9 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
         p.out[(size_t)orow * ncols + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
       } else {
         const float sc = p.row_scale ? p.row_scale[orow] : 1.f;
-        p.out[(size_t)orow * ncols + col] = f32_to_bf16(acc[0][i][q] * sc);
-        p.out[(size_t)orow * ncols + col + kSCols] = f32_to_bf16(acc[1][i][q] * sc);
+        const size_t dst = (size_t)(p.out_rows ? p.out_rows[orow] : orow) * ncols + col;
+        p.out[dst] = f32_to_bf16(acc[0][i][q] * sc);
+        p.out[dst + kSCols] = f32_to_bf16(acc[1][i][q] * sc);
       }
     }
   }
@@ -357,8 +358,9 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
         p.out[(size_t)orow * ncols + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
       } else {
         const float sc = p.row_scale ? p.row_scale[orow] : 1.f;
-        p.out[(size_t)orow * ncols + col] = f32_to_bf16(v[q] * sc);
-        p.out[(size_t)orow * ncols + col + kSCols] = f32_to_bf16(v[4 + q] * sc);
+        const size_t dst = (size_t)(p.out_rows ? p.out_rows[orow] : orow) * ncols + col;
+        p.out[dst] = f32_to_bf16(v[q] * sc);
+        p.out[dst + kSCols] = f32_to_bf16(v[4 + q] * sc);
       }
     }
   }
@@ -545,9 +547,13 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     // down: the tile's row scales through LDS (the first buffer is free once
     // every wave has finished its last stage)
     float* s_scale = reinterpret_cast<float*>(sr0);
+    int* s_orow = reinterpret_cast<int*>(sr0) + BM;
     if (!GATEUP) {
       __syncthreads();
-      if (tid < BM) s_scale[tid] = (p.row_scale && tid < nrows) ? p.row_scale[row0 + tid] : 1.f;
+      if (tid < BM) {
+        s_scale[tid] = (p.row_scale && tid < nrows) ? p.row_scale[row0 + tid] : 1.f;
+        s_orow[tid] = (p.out_rows && tid < nrows) ? p.out_rows[row0 + tid] : row0 + tid;
+      }
       __syncthreads();
     }
 
@@ -559,7 +565,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
         for (int q = 0; q < 4; ++q) {
           const int row = wm * (BM / 2) + 32 * i + 8 * b + 4 * fg + q;
           if (row >= nrows) continue;
-          uint16_t* orow = p.out + (size_t)(row0 + row) * ncols;
+          uint16_t* orow = p.out + (size_t)(GATEUP ? row0 + row : s_orow[row]) * ncols;
           if (GATEUP) {
             const int col = col0 + wn * 32 + fr;
             const float g = acc[i][0][4 * b + q], u = acc[i][1][4 * b + q];

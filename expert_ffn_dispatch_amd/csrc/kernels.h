@@ -56,6 +56,10 @@ struct FfnArgs {
   int rows_total;            // upper bound on rows (N*k)
   int K;                     // contraction: M (phase 1) | H (phase 2)
   int ncols;                 // output columns: H (phase 1) | M (phase 2)
+  // phase 2: if set, sorted row p is stored as row out_rows[p] of `out` (a
+  // token row of the layer output: top-1 routing without shared experts
+  // needs no combine)
+  const int32_t* out_rows = nullptr;
 };
 hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st);
