@@ -71,6 +71,78 @@ def cpu_baseline(w, d):
                       f"(float64 expert math, float32 routing), {dt:.1f} s"}
 
 
+def cost_model(args) -> int:
+    """FinDEP's per-expert cost model (review page, section 核心公式: an expert's
+    time is linear in its batch, t_e(m) = alpha_e + beta_e * m).  For each
+    workload's (M, H, E) it times moe_grouped_ffn (gate+up and down GEMMs)
+    with every one of the E experts given m rows, m = 1, 2, 4, ..., 4096,
+    caches flushed before every call, and fits alpha and beta to the
+    per-expert time (launch time / E) by least squares.  Also reports where a
+    two-line fit (flat weight-streaming part, rising compute part) bends.
+    Weights and rows are seeded normal values drawn on the device (their
+    values do not matter for the timing)."""
+    import torch
+    import expert_ffn_dispatch_amd as moe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    shapes = [("mixtral", 6144, 16384, 8), ("dsv2", 5120, 1536, 160), ("qwen30", 2048, 768, 128),
+              ("qwen235", 4096, 1536, 128)]
+    rows = [1 << i for i in range(13)]
+    reps = 5
+    for i, (name, M, H, E) in enumerate(shapes):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + i)
+
+        def normal(shape, std):
+            return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+        wg = normal((E, H, M), 0.02)
+        wu = normal((E, H, M), 0.02)
+        wd = normal((E, M, H), 0.02)
+        base = normal((rows[-1], M), 1.0)
+        t_us = []
+        for m in rows:
+            A = E * m
+            d = moe.dims(A, M, E, 1, H)
+            off = torch.arange(0, A + 1, m, dtype=torch.int32, device=dev)
+            xs = base[:m].repeat(E, 1)
+            y = torch.empty((A, M), dtype=torch.bfloat16, device=dev)
+            ws = moe.workspace(moe.moe_grouped_ffn_workspace_bytes(d), dev)
+            times = []
+            for r in range(reps):
+                flush.fill_(r & 0xff)
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record()
+                moe.moe_grouped_ffn(d, xs, off, wg, wu, wd, y_sorted=y, ws=ws)
+                ev1.record()
+                torch.cuda.synchronize()
+                times.append(ev0.elapsed_time(ev1) * 1e3)
+            t_us.append(float(np.median(times[1:])) / E)
+            del xs, y, ws
+        mm = np.array(rows, dtype=np.float64)
+        tt = np.array(t_us)
+        beta, alpha = np.polyfit(mm, tt, 1)
+        pred = alpha + beta * mm
+        r2 = 1.0 - float(((tt - pred) ** 2).sum() / ((tt - tt.mean()) ** 2).sum())
+        # bend: where the compute line through the last four points reaches
+        # the flat streaming time of the first five
+        flat = float(tt[:5].mean())
+        b1, a1 = np.polyfit(mm[-4:], tt[-4:], 1)
+        knee = (flat - a1) / b1 if b1 > 0 else None
+        wbytes = 3 * M * H * 2
+        print(json.dumps({"cost_model": name, "M": M, "H": H, "E": E, "rows_per_expert": rows,
+                          "t_us_per_expert": t_us, "alpha_us": float(alpha), "beta_us_per_row": float(beta),
+                          "r2": r2, "flat_us": flat, "knee_rows": float(knee) if knee is not None else None,
+                          "weight_gbs_at_1_row": wbytes / (t_us[0] * 1e-6) / 1e9,
+                          "tflops_at_4096_rows": 6.0 * M * H * rows[-1] / (t_us[-1] * 1e-6) / 1e12}),
+              flush=True)
+        del wg, wu, wd, base
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,11 +157,17 @@ def main() -> int:
     ap.add_argument("--flush", action="store_true",
                     help="overwrite a 1 GiB buffer before every step (outside the per-step events) "
                          "so weights are read from HBM, and report the event-timed layer")
+    ap.add_argument("--cost-model", action="store_true",
+                    help="instead of the layer: time one expert's SwiGLU FFN over per-expert batches "
+                         "1..4096 at each workload's (M, H) and fit t(m) = alpha + beta*m (one JSON "
+                         "line per shape)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs one MoE layer on ONE GPU; --gpus {args.gpus} is not supported "
               f"(the expert-parallel exchange across GPUs is not built)", file=sys.stderr)
         return 2
+    if args.cost_model:
+        return cost_model(args)
 
     import torch
     import expert_ffn_dispatch_amd as moe
@@ -190,7 +268,9 @@ def main() -> int:
         "layer": {"flops": F, "bytes": B, "tflops": F / t_layer / 1e12, "hbm_gbs": B / t_layer / 1e9,
                   "mfma_frac": F / t_layer / (BF16_PEAK_TFLOPS * 1e12), "hbm_frac": B / t_layer / (HBM_PEAK_GBS * 1e9),
                   "roofline_frac": t_roof / t_layer, "t_roof_us": t_roof * 1e6,
-                  "event_layer_us": float(layer_ms.mean() * 1e3)},
+                  "event_layer_us": float(layer_ms.mean() * 1e3),
+                  # per-call spread from the instrumented pass (includes the stage events)
+                  "event_layer_us_p10_p50_p90": [float(np.percentile(layer_ms, q) * 1e3) for q in (10, 50, 90)]},
         "stages_us": {s: float(stage_ms[:, j].mean() * 1e3) for j, s in enumerate(STAGES)},
         "routing": {"active_experts": active, "max_rows": int(counts.max()), "mean_rows": float(counts.mean()),
                     "empty_experts": int((counts == 0).sum())},
