@@ -138,14 +138,21 @@ def gather(x: np.ndarray, sorted_to_assign: np.ndarray, k: int) -> np.ndarray:
 # Experts
 # ----------------------------------------------------------------------------
 
+def weights_f64(w) -> np.ndarray:
+    """Expert weights as float64: bf16 bit patterns (uint16) are widened;
+    anything else (e.g. dequantised FP8 weights) is taken as its values."""
+    w = np.asarray(w)
+    return bf16_to_f64(w) if w.dtype == np.uint16 else w.astype(np.float64)
+
+
 def swiglu(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray):
     """One expert, three GEMMs (FinDEP review, 核心公式: t_e uses 3 GEMMs of
     m_e x M x H): G = X W_g^T, U = X W_u^T, h = silu(G) * U, Y = h W_d^T.
-    X float64 [m, M]; weights bf16 bits, W_g/W_u [H, M], W_d [M, H]."""
-    G = X @ bf16_to_f64(wg).T
-    U = X @ bf16_to_f64(wu).T
+    X float64 [m, M]; weights bf16 bits or float64, W_g/W_u [H, M], W_d [M, H]."""
+    G = X @ weights_f64(wg).T
+    U = X @ weights_f64(wu).T
     h = G / (1.0 + np.exp(-G)) * U
-    return h @ bf16_to_f64(wd).T, h
+    return h @ weights_f64(wd).T, h
 
 
 def grouped_ffn(x_sorted: np.ndarray, offsets: np.ndarray, w_gate, w_up, w_down,
@@ -154,7 +161,7 @@ def grouped_ffn(x_sorted: np.ndarray, offsets: np.ndarray, w_gate, w_up, w_down,
     no work (MoE latency page, section "router 之后还有一串动作")."""
     A, M = np.asarray(x_sorted).shape
     E = len(offsets) - 1
-    H = np.asarray(w_gate).shape[1] if E else 0
+    H = w_gate.shape[1] if E else 0
     y = np.zeros((A, M), np.float64)
     h_all = np.zeros((A, H), np.float64) if keep_h else None
     for e in range(E):
