@@ -35,23 +35,31 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def layer_work(w, active: int):
+def layer_work(w, active: int, fp8: bool = False):
     """Algorithmic flops/bytes of one layer call: three GEMMs of m_e x M x H
     per expert (6*M*H flops per assignment), router, shared experts; bytes =
-    weights of experts that received rows + router + shared weights + x + out."""
+    weights of experts that received rows + router + shared weights + x + out.
+    FP8 weights: one byte per weight plus a float32 scale per output channel."""
     A = w.N * w.k
     has_router = not w.pre_routed
+    wb = 1.0 if fp8 else 2.0
     F = 6.0 * w.M * w.H * A + (2.0 * w.N * w.M * w.E if has_router else 0) + 6.0 * w.M * w.S * w.Hs * w.N
-    B = (active * 3.0 * w.M * w.H * 2 + w.S * 3.0 * w.M * w.Hs * 2 + (w.M * w.E * 2.0 if has_router else 0)
+    B = (active * 3.0 * w.M * w.H * wb + w.S * 3.0 * w.M * w.Hs * wb + (w.M * w.E * 2.0 if has_router else 0)
          + 2.0 * w.N * w.M * 2)
+    if fp8:
+        B += (active * (2.0 * w.H + w.M) + (2.0 * w.S * w.Hs + w.M if w.S else 0)) * 4
     return F, B
 
 
-def gateup_work(w, active: int):
+def gateup_work(w, active: int, fp8: bool = False):
     """Algorithmic bytes/flops of one gate+up launch: W_gate and W_up rows of
-    every active expert, the token rows read once each, h written."""
+    every active expert (and their scales with FP8 weights), the token rows
+    read once each, h written."""
     A = w.N * w.k
-    B = active * 2.0 * w.H * w.M * 2 + w.N * w.M * 2.0 + A * w.H * 2.0
+    wb = 1.0 if fp8 else 2.0
+    B = active * 2.0 * w.H * w.M * wb + w.N * w.M * 2.0 + A * w.H * 2.0
+    if fp8:
+        B += active * 2.0 * w.H * 4
     F = 4.0 * w.M * w.H * A
     return F, B
 
@@ -157,6 +165,10 @@ def main() -> int:
     ap.add_argument("--flush", action="store_true",
                     help="overwrite a 1 GiB buffer before every step (outside the per-step events) "
                          "so weights are read from HBM, and report the event-timed layer")
+    ap.add_argument("--fp8", action="store_true",
+                    help="run moe_layer_fp8: expert weights quantised once (moe_quantize_fp8, OCP E4M3 "
+                         "with per-channel scales) before timing; activations and h stay bf16; no CPU "
+                         "baseline in this mode")
     ap.add_argument("--cost-model", action="store_true",
                     help="instead of the layer: time one expert's SwiGLU FFN over per-expert batches "
                          "1..4096 at each workload's (M, H) and fit t(m) = alpha + beta*m (one JSON "
@@ -198,10 +210,21 @@ def main() -> int:
         ids = torch.empty((w.N, w.k), dtype=torch.int32, device=dev)
         wts = torch.empty((w.N, w.k), dtype=torch.float32, device=dev)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+    if args.fp8:
+        W8 = moe.quantize_ffn_fp8(T["w_gate"], T["w_up"], T["w_down"])
+        S8 = moe.quantize_ffn_fp8(T["ws_gate"], T["ws_up"], T["ws_down"]) if w.S > 0 else None
+        for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            T.pop(n, None)       # the bf16 expert weights are not used in this mode
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
 
     def step(events=None):
         if events is not None:
             moe.moe_set_stage_events(events)
+        if args.fp8:
+            moe.moe_layer_fp8(dm, T["x"], W8, S8, w_router=T.get("w_router"), router_bias=T.get("router_bias"),
+                              topk_ids=ids, topk_weights=wts, ids_in=w.pre_routed, out=out, ws=ws)
+            return
         moe.moe_layer(dm, T["x"], T["w_gate"], T["w_up"], T["w_down"], w_router=T.get("w_router"),
                       router_bias=T.get("router_bias"), ws_gate=T.get("ws_gate"), ws_up=T.get("ws_up"),
                       ws_down=T.get("ws_down"), topk_ids=ids, topk_weights=wts, ids_in=w.pre_routed,
@@ -242,8 +265,8 @@ def main() -> int:
     hid = ids.cpu().numpy().reshape(-1)
     counts = np.bincount(hid, minlength=w.E)
     active = int((counts > 0).sum())
-    F, B = layer_work(w, active)
-    Fg, Bg = gateup_work(w, active)
+    F, B = layer_work(w, active, args.fp8)
+    Fg, Bg = gateup_work(w, active, args.fp8)
     t_gu = stage_ms[:, 3].mean() * 1e-3
     # the gate+up launch is bound by MFMA when its flops per algorithmic
     # byte exceed the ridge point (peak flops / peak bandwidth), else by HBM
@@ -257,6 +280,7 @@ def main() -> int:
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.title, "N": w.N, "M": w.M, "E": w.E, "k": w.k, "H": w.H, "S": w.S, "Hs": w.Hs,
+                   "expert_weights": "fp8 e4m3, per-channel fp32 scales" if args.fp8 else "bf16",
                    "parallelism": "single GPU", "timing": "event-timed, caches flushed" if args.flush
                    else "wall clock over back-to-back steps"},
         "roofline": {"bound": "mfma" if mfma_bound else "hbm",
@@ -290,10 +314,11 @@ def main() -> int:
         torch.cuda.synchronize()
         res["copy_gbs"] = 2.0 * n * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
         del src, dst
-    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{w.name}_N{w.N}.txt"))
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles",
+                                             f"traffic_{w.name}_N{w.N}{'_fp8' if args.fp8 else ''}.txt"))
     if tr is not None:
         res["roofline"]["traffic"] = float(tr["traffic_bytes"])
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fp8:
         log("bench: timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, d)
     print(json.dumps(res), flush=True)

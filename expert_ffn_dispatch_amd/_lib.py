@@ -19,7 +19,7 @@ EXPORTS = (
     "moe_abi_version", "moe_last_error", "moe_layer_workspace_bytes", "moe_route_workspace_bytes",
     "moe_permute_workspace_bytes",
     "moe_grouped_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-    "moe_layer", "moe_set_stage_events",
+    "moe_layer", "moe_set_stage_events", "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_layer_fp8",
 )
 MOE_STAGE_EVENTS = 7
 
@@ -27,6 +27,11 @@ MOE_STAGE_EVENTS = 7
 class MoeDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_tokens", "hidden", "n_experts", "top_k", "expert_width", "n_shared", "shared_width")]
+
+
+class MoeFp8Ffn(ctypes.Structure):
+    """struct moe_fp8_ffn: device pointers of E4M3 codes and per-channel scales."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("gate", "up", "down", "gate_scale", "up_scale", "down_scale")]
 
 
 class MoeError(RuntimeError):
@@ -60,6 +65,10 @@ def load() -> ctypes.CDLL:
     lib.moe_combine.argtypes = [DIMS, P, P, P, P, P, P]
     lib.moe_layer.argtypes = [DIMS, ctypes.c_uint32] + [P] * 13 + [ctypes.c_size_t, P]
     lib.moe_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    F8 = ctypes.POINTER(MoeFp8Ffn)
+    lib.moe_quantize_fp8.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, P]
+    lib.moe_grouped_ffn_fp8.argtypes = [DIMS, P, P, F8, P, P, P, ctypes.c_size_t, P]
+    lib.moe_layer_fp8.argtypes = [DIMS, ctypes.c_uint32, P, P, P, F8, F8, P, P, P, P, ctypes.c_size_t, P]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib

@@ -146,6 +146,79 @@ def moe_layer(d: MoeDims, x, w_gate, w_up, w_down, w_router=None, router_bias=No
     return out
 
 
+class Fp8Weights:
+    """FP8 (OCP E4M3) expert weights with one float32 scale per output channel:
+    codes `gate`/`up` [E][H][M] and `down` [E][M][H] (torch.uint8), scales
+    `gate_scale`/`up_scale` [E][H] and `down_scale` [E][M] (torch.float32)."""
+
+    FIELDS = ("gate", "up", "down", "gate_scale", "up_scale", "down_scale")
+
+    def __init__(self, gate, up, down, gate_scale, up_scale, down_scale):
+        self.gate, self.up, self.down = gate, up, down
+        self.gate_scale, self.up_scale, self.down_scale = gate_scale, up_scale, down_scale
+
+    def c_struct(self) -> _lib.MoeFp8Ffn:
+        codes = [_ptr(getattr(self, n), (torch.uint8,)) for n in self.FIELDS[:3]]
+        scales = [_ptr(getattr(self, n), (torch.float32,)) for n in self.FIELDS[3:]]
+        return _lib.MoeFp8Ffn(*codes, *scales)
+
+
+def moe_quantize_fp8(w, q=None, scale=None, stream=None):
+    """Per-output-channel E4M3 quantisation of a bf16 matrix [..., cols]
+    (every leading index is one output channel).  Returns (codes, scales)."""
+    rows = w.numel() // w.shape[-1]
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if scale is None:
+        scale = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    _lib.check(_lib.load().moe_quantize_fp8(_ptr(w, _BF16_LIKE), rows, w.shape[-1], _ptr(q, (torch.uint8,)),
+                                            _ptr(scale, (torch.float32,)), _stream(stream)))
+    return q, scale
+
+
+def quantize_ffn_fp8(w_gate, w_up, w_down, stream=None) -> Fp8Weights:
+    """FP8 copies of one set of expert weights (three moe_quantize_fp8 calls)."""
+    g, sg = moe_quantize_fp8(w_gate, stream=stream)
+    u, su = moe_quantize_fp8(w_up, stream=stream)
+    d, sd = moe_quantize_fp8(w_down, stream=stream)
+    return Fp8Weights(g, u, d, sg, su, sd)
+
+
+def moe_grouped_ffn_fp8(d: MoeDims, x_sorted, expert_offsets, experts: Fp8Weights, row_scale=None,
+                        y_sorted=None, ws=None, stream=None):
+    dev = x_sorted.device
+    A = d.n_tokens * d.top_k
+    if y_sorted is None:
+        y_sorted = torch.empty((A, d.hidden), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(moe_grouped_ffn_workspace_bytes(d), dev)
+    st = experts.c_struct()
+    _lib.check(_lib.load().moe_grouped_ffn_fp8(ctypes.byref(d), _ptr(x_sorted, _BF16_LIKE),
+                                               _ptr(expert_offsets, (torch.int32,)), ctypes.byref(st),
+                                               _ptr(row_scale, (torch.float32,)), _ptr(y_sorted, _BF16_LIKE),
+                                               _ptr(ws), ws.numel(), _stream(stream)))
+    return y_sorted
+
+
+def moe_layer_fp8(d: MoeDims, x, experts: Fp8Weights, shared: Optional[Fp8Weights] = None, w_router=None,
+                  router_bias=None, topk_ids=None, topk_weights=None, ids_in: bool = False, out=None, ws=None,
+                  stream=None):
+    dev = x.device
+    flags = MOE_FLAG_IDS_IN if ids_in else 0
+    if out is None:
+        out = torch.empty((d.n_tokens, d.hidden), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(moe_layer_workspace_bytes(d, flags), dev)
+    ex = experts.c_struct()
+    sh = shared.c_struct() if shared is not None else None
+    _lib.check(_lib.load().moe_layer_fp8(
+        ctypes.byref(d), flags, _ptr(x, _BF16_LIKE), _ptr(w_router, _BF16_LIKE),
+        _ptr(router_bias, (torch.float32,)), ctypes.byref(ex), ctypes.byref(sh) if sh is not None else None,
+        _ptr(topk_ids, (torch.int32,)), _ptr(topk_weights, (torch.float32,)), _ptr(out, _BF16_LIKE),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
 def moe_set_stage_events(events) -> None:
     """Record the given MOE_STAGE_EVENTS torch.cuda.Event objects at the stage
     boundaries of the next moe_layer call on this thread (None clears).  The

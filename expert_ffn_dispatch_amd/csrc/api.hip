@@ -166,6 +166,219 @@ int check_ws(const char* fn, void* ws, size_t ws_bytes, size_t need) {
   return MOE_OK;
 }
 
+// Expert weights of one call: bf16 matrices, or FP8 codes with per-channel
+// scales (then the bf16 pointers are NULL).
+struct ExpertWeights {
+  const uint16_t* gate = nullptr;
+  const uint16_t* up = nullptr;
+  const uint16_t* down = nullptr;
+  const uint8_t* qgate = nullptr;
+  const uint8_t* qup = nullptr;
+  const uint8_t* qdown = nullptr;
+  const float* sgate = nullptr;
+  const float* sup = nullptr;
+  const float* sdown = nullptr;
+};
+
+ExpertWeights bf16_weights(const moe_bf16* g, const moe_bf16* u, const moe_bf16* d) {
+  ExpertWeights w;
+  w.gate = g;
+  w.up = u;
+  w.down = d;
+  return w;
+}
+
+ExpertWeights fp8_weights(const moe_fp8_ffn* f) {
+  ExpertWeights w;
+  if (f == nullptr) return w;
+  w.qgate = f->gate;
+  w.qup = f->up;
+  w.qdown = f->down;
+  w.sgate = f->gate_scale;
+  w.sup = f->up_scale;
+  w.sdown = f->down_scale;
+  return w;
+}
+
+moe::FfnArgs gateup_args(const ExpertWeights& w) {
+  moe::FfnArgs a{};
+  a.w0 = w.gate;
+  a.w1 = w.up;
+  a.q0 = w.qgate;
+  a.q1 = w.qup;
+  a.s0 = w.sgate;
+  a.s1 = w.sup;
+  return a;
+}
+
+moe::FfnArgs down_args(const ExpertWeights& w) {
+  moe::FfnArgs a{};
+  a.w0 = w.down;
+  a.q0 = w.qdown;
+  a.s0 = w.sdown;
+  return a;
+}
+
+// An FP8 weight set: every pointer present and aligned.
+int check_fp8_ffn(const char* fn, const char* which, const moe_fp8_ffn* f) {
+  if (f == nullptr) return fail(MOE_ERR_INVALID, "%s: %s is NULL", fn, which);
+  const void* ptrs[6] = {f->gate, f->up, f->down, f->gate_scale, f->up_scale, f->down_scale};
+  const char* names[6] = {"gate", "up", "down", "gate_scale", "up_scale", "down_scale"};
+  for (int i = 0; i < 6; ++i) {
+    if (ptrs[i] == nullptr) return fail(MOE_ERR_INVALID, "%s: %s->%s is NULL", fn, which, names[i]);
+    if (!aligned(ptrs[i])) return fail(MOE_ERR_INVALID, "%s: %s->%s is not 16-byte aligned", fn, which, names[i]);
+  }
+  return MOE_OK;
+}
+
+// The FP8 kernels walk the contraction in 256-element chunks.
+int check_fp8_dims(const char* fn, const moe_dims* d) {
+  if (d->hidden % 256 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 weights need hidden %% 256 == 0 (hidden=%d)", fn, d->hidden);
+  if (d->expert_width % 256 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 weights need expert_width %% 256 == 0 (expert_width=%d)", fn,
+                d->expert_width);
+  if (d->n_shared > 0 && (d->n_shared * d->shared_width) % 256 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 weights need n_shared*shared_width %% 256 == 0", fn);
+  return MOE_OK;
+}
+
+// Both grouped GEMM phases; the arguments have been checked.
+int run_grouped_ffn(const char* fn, const moe_dims* dims, const moe_bf16* x_sorted, const int32_t* expert_offsets,
+                    const ExpertWeights& wt, const float* row_scale, moe_bf16* y_sorted, void* ws,
+                    hipStream_t st) {
+  const int ncu = num_cus();
+  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
+  const int A = dims->n_tokens * dims->top_k;
+  uint16_t* h = static_cast<uint16_t*>(ws);
+  moe::FfnArgs g = gateup_args(wt);
+  g.a = x_sorted;
+  g.offsets = expert_offsets;
+  g.out = h;
+  g.E = dims->n_experts;
+  g.rows_total = A;
+  g.K = dims->hidden;
+  g.ncols = dims->expert_width;
+  if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
+  moe::FfnArgs dn = down_args(wt);
+  dn.a = h;
+  dn.offsets = expert_offsets;
+  dn.row_scale = row_scale;
+  dn.out = y_sorted;
+  dn.E = dims->n_experts;
+  dn.rows_total = A;
+  dn.K = dims->expert_width;
+  dn.ncols = dims->hidden;
+  if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  return ok();
+}
+
+// The whole layer; the weight pointers have been checked by the caller.
+int run_layer(const char* fn, const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,
+              const float* router_bias, const ExpertWeights& routed, const ExpertWeights& shared,
+              int32_t* topk_ids, float* topk_weights, moe_bf16* out, void* ws, size_t ws_bytes,
+              moe_stream stream) {
+  if (flags & ~uint32_t(MOE_FLAG_IDS_IN)) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+  const bool ids_in = (flags & MOE_FLAG_IDS_IN) != 0;
+  REQ_PTR(x);
+  if (ids_in) {
+    if (w_router != nullptr || router_bias != nullptr)
+      return fail(MOE_ERR_INVALID, "%s: w_router/router_bias must be NULL with MOE_FLAG_IDS_IN", fn);
+    REQ_PTR(topk_ids);
+    REQ_PTR(topk_weights);
+  } else {
+    REQ_PTR(w_router);
+    OPT_PTR(router_bias);
+    OPT_PTR(topk_ids);
+    OPT_PTR(topk_weights);
+  }
+  REQ_PTR(out);
+  Carver sz(nullptr);
+  carve_layer(sz, *dims);
+  if (int r = check_ws(fn, ws, ws_bytes, sz.off)) return r;
+  const int ncu = num_cus();
+  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
+
+  Carver c(ws);
+  LayerWs w = carve_layer(c, *dims);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int N = dims->n_tokens, M = dims->hidden, E = dims->n_experts, k = dims->top_k, H = dims->expert_width;
+  const int A = N * k;
+  int32_t* ids = topk_ids ? topk_ids : w.ids;
+  float* wts = topk_weights ? topk_weights : w.wts;
+  const bool rec = g_stage_on;
+  g_stage_on = false;
+  auto mark = [&](int i) -> hipError_t { return rec ? hipEventRecord(g_stage_ev[i], st) : hipSuccess; };
+  if (hipError_t e = mark(0)) return device_error(fn, e);
+
+  if (!ids_in) {
+    moe::RouteArgs r{x, w_router, router_bias, N, M, E, k, ids, wts};
+    if (hipError_t e = moe::launch_route(r, w.route, st)) return device_error(fn, e);
+  }
+  if (hipError_t e = mark(1)) return device_error(fn, e);
+  moe::PermuteArgs p{ids, A, E, k, w.counts, w.offsets, w.s2a, w.a2s, w.row_token, wts, w.row_weight,
+                     w.perm.tile_hist, w.perm.tile_off};
+  if (hipError_t e = moe::launch_permute(p, st)) return device_error(fn, e);
+  if (hipError_t e = mark(2)) return device_error(fn, e);
+
+  if (dims->n_shared > 0) {
+    const int SH = dims->n_shared * dims->shared_width;
+    moe::FfnArgs g = gateup_args(shared);
+    g.a = x;
+    g.fixed_rows = N;
+    g.out = w.hs;
+    g.E = 1;
+    g.rows_total = N;
+    g.K = M;
+    g.ncols = SH;
+    if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
+    moe::FfnArgs dn = down_args(shared);
+    dn.a = w.hs;
+    dn.fixed_rows = N;
+    dn.out = w.ys;
+    dn.E = 1;
+    dn.rows_total = N;
+    dn.K = SH;
+    dn.ncols = M;
+    if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  }
+  if (hipError_t e = mark(3)) return device_error(fn, e);
+  moe::FfnArgs g = gateup_args(routed);
+  g.a = x;
+  g.a_rows = w.row_token;
+  g.offsets = w.offsets;
+  g.out = w.h;
+  g.E = E;
+  g.rows_total = A;
+  g.K = M;
+  g.ncols = H;
+  if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
+  if (hipError_t e = mark(4)) return device_error(fn, e);
+  // top-1 routing without shared experts: every token has exactly one row,
+  // so the down GEMM stores it straight into the output (the combine would
+  // only copy it)
+  const bool direct = (k == 1 && dims->n_shared == 0);
+  moe::FfnArgs dn = down_args(routed);
+  dn.a = w.h;
+  dn.offsets = w.offsets;
+  dn.row_scale = w.row_weight;
+  dn.out = direct ? out : w.y;
+  dn.E = E;
+  dn.rows_total = A;
+  dn.K = H;
+  dn.ncols = M;
+  dn.out_rows = direct ? w.row_token : nullptr;
+  if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  if (hipError_t e = mark(5)) return device_error(fn, e);
+
+  if (!direct) {
+    moe::CombineArgs cb{w.y, w.a2s, nullptr, w.ys, out, N, M, k};
+    if (hipError_t e = moe::launch_combine(cb, st)) return device_error(fn, e);
+  }
+  if (hipError_t e = mark(6)) return device_error(fn, e);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,17 +503,40 @@ int moe_grouped_ffn(const moe_dims* dims, const moe_bf16* x_sorted, const int32_
   size_t need = 0;
   moe_grouped_ffn_workspace_bytes(dims, &need);
   if (int r = check_ws(fn, ws, ws_bytes, need)) return r;
-  const int ncu = num_cus();
-  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
-  const int A = dims->n_tokens * dims->top_k;
-  uint16_t* h = static_cast<uint16_t*>(ws);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  moe::FfnArgs g{x_sorted, nullptr, expert_offsets, 0, w_gate, w_up, nullptr, h,
-                 dims->n_experts, A, dims->hidden, dims->expert_width};
-  if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
-  moe::FfnArgs dn{h, nullptr, expert_offsets, 0, w_down, nullptr, row_scale, y_sorted,
-                  dims->n_experts, A, dims->expert_width, dims->hidden};
-  if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  return run_grouped_ffn(fn, dims, x_sorted, expert_offsets, bf16_weights(w_gate, w_up, w_down), row_scale,
+                         y_sorted, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_grouped_ffn_fp8(const moe_dims* dims, const moe_bf16* x_sorted, const int32_t* expert_offsets,
+                        const moe_fp8_ffn* experts, const float* row_scale, moe_bf16* y_sorted, void* ws,
+                        size_t ws_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn_fp8";
+  if (int r = check_dims(fn, dims, true)) return r;
+  if (int r = check_fp8_dims(fn, dims)) return r;
+  REQ_PTR(x_sorted);
+  REQ_PTR(expert_offsets);
+  if (int r = check_fp8_ffn(fn, "experts", experts)) return r;
+  OPT_PTR(row_scale);
+  REQ_PTR(y_sorted);
+  size_t need = 0;
+  moe_grouped_ffn_workspace_bytes(dims, &need);
+  if (int r = check_ws(fn, ws, ws_bytes, need)) return r;
+  return run_grouped_ffn(fn, dims, x_sorted, expert_offsets, fp8_weights(experts), row_scale, y_sorted, ws,
+                         static_cast<hipStream_t>(stream));
+}
+
+int moe_quantize_fp8(const moe_bf16* w, int64_t rows, int32_t cols, moe_fp8* q, float* scale,
+                     moe_stream stream) {
+  const char* fn = "moe_quantize_fp8";
+  if (rows < 1 || rows > (int64_t(1) << 26))
+    return fail(MOE_ERR_INVALID, "%s: rows=%lld outside [1, 2^26]", fn, (long long)rows);
+  if (cols < 64 || cols > 65536 || cols % 64 != 0)
+    return fail(MOE_ERR_INVALID, "%s: cols=%d must be a multiple of 64 in [64, 65536]", fn, cols);
+  REQ_PTR(w);
+  REQ_PTR(q);
+  REQ_PTR(scale);
+  if (hipError_t e = moe::launch_quantize_fp8(w, rows, cols, q, scale, static_cast<hipStream_t>(stream)))
+    return device_error(fn, e);
   return ok();
 }
 
@@ -325,20 +561,6 @@ int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe
               float* topk_weights, moe_bf16* out, void* ws, size_t ws_bytes, moe_stream stream) {
   const char* fn = "moe_layer";
   if (int r = check_dims(fn, dims, true)) return r;
-  if (flags & ~uint32_t(MOE_FLAG_IDS_IN)) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
-  const bool ids_in = (flags & MOE_FLAG_IDS_IN) != 0;
-  REQ_PTR(x);
-  if (ids_in) {
-    if (w_router != nullptr || router_bias != nullptr)
-      return fail(MOE_ERR_INVALID, "%s: w_router/router_bias must be NULL with MOE_FLAG_IDS_IN", fn);
-    REQ_PTR(topk_ids);
-    REQ_PTR(topk_weights);
-  } else {
-    REQ_PTR(w_router);
-    OPT_PTR(router_bias);
-    OPT_PTR(topk_ids);
-    OPT_PTR(topk_weights);
-  }
   REQ_PTR(w_gate);
   REQ_PTR(w_up);
   REQ_PTR(w_down);
@@ -349,61 +571,25 @@ int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe
   } else if (ws_gate || ws_up || ws_down) {
     return fail(MOE_ERR_INVALID, "%s: shared-expert weights given with n_shared = 0", fn);
   }
-  REQ_PTR(out);
-  Carver sz(nullptr);
-  carve_layer(sz, *dims);
-  if (int r = check_ws(fn, ws, ws_bytes, sz.off)) return r;
-  const int ncu = num_cus();
-  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
+  return run_layer(fn, dims, flags, x, w_router, router_bias, bf16_weights(w_gate, w_up, w_down),
+                   bf16_weights(ws_gate, ws_up, ws_down), topk_ids, topk_weights, out, ws, ws_bytes, stream);
+}
 
-  Carver c(ws);
-  LayerWs w = carve_layer(c, *dims);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int N = dims->n_tokens, M = dims->hidden, E = dims->n_experts, k = dims->top_k, H = dims->expert_width;
-  const int A = N * k;
-  int32_t* ids = topk_ids ? topk_ids : w.ids;
-  float* wts = topk_weights ? topk_weights : w.wts;
-  const bool rec = g_stage_on;
-  g_stage_on = false;
-  auto mark = [&](int i) -> hipError_t { return rec ? hipEventRecord(g_stage_ev[i], st) : hipSuccess; };
-  if (hipError_t e = mark(0)) return device_error(fn, e);
-
-  if (!ids_in) {
-    moe::RouteArgs r{x, w_router, router_bias, N, M, E, k, ids, wts};
-    if (hipError_t e = moe::launch_route(r, w.route, st)) return device_error(fn, e);
-  }
-  if (hipError_t e = mark(1)) return device_error(fn, e);
-  moe::PermuteArgs p{ids, A, E, k, w.counts, w.offsets, w.s2a, w.a2s, w.row_token, wts, w.row_weight,
-                     w.perm.tile_hist, w.perm.tile_off};
-  if (hipError_t e = moe::launch_permute(p, st)) return device_error(fn, e);
-  if (hipError_t e = mark(2)) return device_error(fn, e);
-
+int moe_layer_fp8(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,
+                  const float* router_bias, const moe_fp8_ffn* experts, const moe_fp8_ffn* shared,
+                  int32_t* topk_ids, float* topk_weights, moe_bf16* out, void* ws, size_t ws_bytes,
+                  moe_stream stream) {
+  const char* fn = "moe_layer_fp8";
+  if (int r = check_dims(fn, dims, true)) return r;
+  if (int r = check_fp8_dims(fn, dims)) return r;
+  if (int r = check_fp8_ffn(fn, "experts", experts)) return r;
   if (dims->n_shared > 0) {
-    const int SH = dims->n_shared * dims->shared_width;
-    moe::FfnArgs g{x, nullptr, nullptr, N, ws_gate, ws_up, nullptr, w.hs, 1, N, M, SH};
-    if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
-    moe::FfnArgs dn{w.hs, nullptr, nullptr, N, ws_down, nullptr, nullptr, w.ys, 1, N, SH, M};
-    if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+    if (int r = check_fp8_ffn(fn, "shared", shared)) return r;
+  } else if (shared != nullptr) {
+    return fail(MOE_ERR_INVALID, "%s: shared-expert weights given with n_shared = 0", fn);
   }
-  if (hipError_t e = mark(3)) return device_error(fn, e);
-  moe::FfnArgs g{x, w.row_token, w.offsets, 0, w_gate, w_up, nullptr, w.h, E, A, M, H};
-  if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
-  if (hipError_t e = mark(4)) return device_error(fn, e);
-  // top-1 routing without shared experts: every token has exactly one row,
-  // so the down GEMM stores it straight into the output (the combine would
-  // only copy it)
-  const bool direct = (k == 1 && dims->n_shared == 0);
-  moe::FfnArgs dn{w.h, nullptr, w.offsets, 0, w_down, nullptr, w.row_weight, direct ? out : w.y, E, A, H, M,
-                  direct ? w.row_token : nullptr};
-  if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
-  if (hipError_t e = mark(5)) return device_error(fn, e);
-
-  if (!direct) {
-    moe::CombineArgs cb{w.y, w.a2s, nullptr, w.ys, out, N, M, k};
-    if (hipError_t e = moe::launch_combine(cb, st)) return device_error(fn, e);
-  }
-  if (hipError_t e = mark(6)) return device_error(fn, e);
-  return ok();
+  return run_layer(fn, dims, flags, x, w_router, router_bias, fp8_weights(experts), fp8_weights(shared),
+                   topk_ids, topk_weights, out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

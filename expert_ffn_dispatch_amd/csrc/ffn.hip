@@ -27,6 +27,8 @@
 //    L2.
 // Both walk a tile list built in LDS from the device-side group offsets, so
 // the host never reads the counts.
+#include <type_traits>
+
 #include "ffn_common.h"
 
 namespace moe {
@@ -40,34 +42,84 @@ namespace {
 // request stream dense (an MFMA-fragment-shaped load touches 16 rows x 64 B
 // and streams markedly slower).  Each wave owns 16 output columns; its
 // weight chunks are prefetched LA = 2 chunks ahead into registers, then
-// staged through a wave-private LDS slot (16-byte chunks XOR-swizzled by row)
+// staged through a wave-private LDS slot (16-byte pieces XOR-swizzled by row)
 // from which the MFMA fragments are read.  Only the token rows (A) are shared
 // by the block's four waves: double-buffered in LDS, one barrier per chunk.
+//
+// A chunk is 256 bytes of every weight row: 128 bf16 weights, or 256 FP8
+// (OCP E4M3) codes.  FP8 codes are widened to bf16 as the MFMA fragments are
+// read from LDS (exactly: every E4M3 value is a bf16 value), the products
+// run on the bf16 MFMA, and the per-output-channel scale multiplies the fp32
+// sum in the epilogue, so a weight row costs half the HBM bytes.
 
-constexpr int kSK = 128;   // k per chunk: 256 B of every weight row
-constexpr int kSCols = 16; // output columns per wave
+constexpr int kSK = 128;     // 16-bit elements per 256-byte weight-row chunk
+constexpr int kSCols = 16;   // output columns per wave
+constexpr int kRowBytes = 256;
+
+// Eight E4M3 codes (the bytes of lo, then hi, in k order) -> eight bf16.
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  return r;
+}
+
+// B fragment of MFMA sub-step s from a wave's 16-row weight slot (256 bytes
+// per row, 16-byte piece c of row r at piece c ^ r): lane l supplies row
+// l & 15 and the eight contraction elements 8 (l >> 4) .. +7 of the step.
+template <bool F8>
+__device__ __forceinline__ u32x4_t weight_fragment(const uint16_t* slot, int s, int lane) {
+  const int fr = lane & 15, g = lane >> 4;
+  if constexpr (F8) {
+    const int piece = 2 * s + (g >> 1);          // bytes 32 s + 8 g of the row
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(slot) + fr * kRowBytes + ((piece ^ fr) << 4) + ((g & 1) << 3);
+    const uint2 raw = *reinterpret_cast<const uint2*>(p);
+    return e4m3x8_to_bf16x8(raw.x, raw.y);
+  } else {
+    const int piece = 4 * s + g;
+    return *reinterpret_cast<const u32x4_t*>(slot + fr * kSK + ((piece ^ fr) << 3));
+  }
+}
+
 // LA: weight chunks in flight per wave (registers).  NMD: 16-row groups per
-// wave for down (2 or 3).
-template <int FM, bool GATEUP, int LA, int NMD>
-__global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
+// wave for down (2 or 3).  F8: E4M3 weights with per-channel scales.  NW:
+// waves per block (4 or 8); the token rows a block stages serve all of its
+// waves, so 8 waves halve the token-row reads per weight byte.
+template <int FM, bool GATEUP, int LA, int NMD, bool F8, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_stream_kernel(FfnArgs p) {
   constexpr int RB = FM * 16;
+  constexpr int KC = F8 ? 2 * kSK : kSK;     // contraction elements per chunk
+  constexpr int ACH = KC / 8;                // 16-byte pieces of a token row per chunk
+  constexpr int NSUB = KC / 32;              // MFMA sub-steps per chunk
+  // Token rows: bf16 weights double-buffer them (one barrier per chunk);
+  // FP8 chunks are twice as long in k, so one buffer (two barriers per
+  // chunk) keeps the LDS at two blocks per CU.  Either way the wait for the
+  // next chunk's token rows, issued before this chunk's weight prefetch,
+  // leaves the prefetch a whole chunk to land (vector loads complete in
+  // order, so waiting for a load waits for every older one).
+  constexpr int NABUF = F8 ? 1 : 2;
+  using ARow = typename std::conditional<F8, u32x4_t, uint4>::type;
   // every wave streams groups of 16 weight rows: gate and up rows of the
   // same 16 h columns, or (down) NMD x 16 consecutive rows of W_down, i.e.
   // 16 * NMD output columns (measured on the Mixtral-shaped down: 48 columns
   // per wave, 256 blocks, ran 9% faster than 32 columns per wave)
   constexpr int NMAT = GATEUP ? 2 : NMD;
   constexpr int WCOLS = GATEUP ? kSCols : NMD * kSCols;   // output columns per wave
-  constexpr int BNC = 4 * WCOLS;
-  constexpr int AL = RB * 16 / 256;          // A uint4 per thread per chunk
-  __shared__ __align__(16) uint16_t sa[2][RB * kSK];
-  __shared__ __align__(16) uint16_t sb[4][NMAT][kSCols * kSK];
+  constexpr int BNC = NW * WCOLS;
+  constexpr int NTH = 64 * NW;
+  constexpr int AL = (RB * ACH + NTH - 1) / NTH;   // A pieces per thread per chunk (the last may be partial)
+  constexpr bool AFULL = RB * ACH % NTH == 0;
+  __shared__ __align__(16) uint16_t sa[NABUF][RB * KC];
+  __shared__ __align__(16) uint16_t sb[NW][NMAT][kSCols * kSK];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tp[kMaxGroups + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = p.K, ncols = p.ncols;
   const int NT = ncols / BNC;
-  const int NC = K / kSK;                     // the host sends only K % 128 == 0 here
+  const int NC = K / KC;                      // the host sends only K % KC == 0 here
   // one tile = (group, pass of RB rows, 64 output columns); one tile per block
   const int total = build_tile_list<RB>(p, NT, s_off, s_tp);
   // Tiles follow the block index.  (Dealing one expert's tiles to a single
@@ -83,25 +135,28 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
   const int row0 = s_off[e] + rt * RB;
   const int nrows = min(RB, cnt - rt * RB);
   const int col0 = ct * BNC + wave * WCOLS;
-  // element offset of the block's c-th chunk: each block starts its k walk
-  // at a different chunk (wrapping), so the blocks running together spread
-  // over the offsets within the weight rows.  Measured: with every block at
-  // the same offset, gate+up streamed ~10% slower whenever the gate and up
-  // tensors sat at unfavourable relative addresses.
+  // the block's c-th chunk: each block starts its k walk at a different
+  // chunk (wrapping), so the blocks running together spread over the
+  // offsets within the weight rows.  Measured: with every block at the same
+  // offset, gate+up streamed ~10% slower whenever the gate and up tensors
+  // sat at unfavourable relative addresses.
   const int rot = (int)(blockIdx.x % (unsigned)NC);
-  auto kof = [rot, NC](int c) {
+  auto kc = [rot, NC](int c) {
     const int cc = c + rot;
-    return (cc >= NC ? cc - NC : cc) * kSK;
+    return cc >= NC ? cc - NC : cc;
   };
 
-  // weight load mapping: instruction i covers rows 4i + (lane >> 4), 16-byte chunk lane & 15
+  // weight load mapping: instruction i covers rows 4i + (lane >> 4), 16-byte piece lane & 15
   const int brow = lane >> 4, bch = lane & 15;
-  const size_t wrow = ((size_t)e * ncols + col0 + brow) * K + bch * 8;
-  const uint16_t* wb0 = p.w0 + wrow;
-  const uint16_t* wb1 = GATEUP ? p.w1 + wrow : p.w0 + wrow + (size_t)kSCols * K;
+  const size_t RP = (size_t)K * (F8 ? 1 : 2);                 // weight row pitch in bytes
+  const uint8_t* w0b = F8 ? p.q0 : reinterpret_cast<const uint8_t*>(p.w0);
+  const uint8_t* w1b = F8 ? p.q1 : reinterpret_cast<const uint8_t*>(p.w1);
+  const size_t wrow = ((size_t)e * ncols + col0 + brow) * RP + bch * 16;
+  const uint8_t* wb0 = w0b + wrow;
+  const uint8_t* wb1 = GATEUP ? w1b + wrow : wb0 + (size_t)kSCols * RP;
   // weight group m: gate / up rows, or down rows 16m.. of the wave's columns
-  auto wsrc = [&](int m) -> const uint16_t* {
-    return GATEUP ? (m == 0 ? wb0 : wb1) : wb0 + (size_t)m * kSCols * K;
+  auto wsrc = [&](int m) -> const uint8_t* {
+    return GATEUP ? (m == 0 ? wb0 : wb1) : wb0 + (size_t)m * kSCols * RP;
   };
   int bdst[4];
 #pragma unroll
@@ -115,11 +170,11 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
   int adst[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int r = (tid >> 4) + 16 * i, ch = tid & 15;
+    const int r = tid / ACH + (NTH / ACH) * i, ch = tid % ACH;
     const int rr = (r < nrows) ? r : 0;
     const int grow = p.a_rows ? p.a_rows[row0 + rr] : (row0 + rr);
     aoff[i] = (uint32_t)grow * (uint32_t)K + ch * 8;
-    adst[i] = r * kSK + ((ch ^ (r & 15)) << 3);
+    adst[i] = r * KC + ((ch ^ (r & 15)) << 3);
   }
   f32x4_t acc[NMAT][FM];
 #pragma unroll
@@ -127,79 +182,110 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) acc[m][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: chunk 0 straight into LDS, chunks 1..LA into registers
-  uint4 bq[LA][NMAT][4];
+  // prologue: chunk 0 straight into LDS, chunks 1..LA into registers.
+  // FP8 walks the chunks LA at a time with set u of bq holding chunk c+1 at
+  // chunk c = c0 + u (no register copies); bf16 shifts the sets down by one
+  // each chunk (measured: the copies cost FP8 ~6% and save bf16 ~4%).
+  using WRow = typename std::conditional<F8, u32x4_t, uint4>::type;
+  constexpr int UN = F8 ? LA : 1;            // chunks per trip of the loop
+  WRow bq[LA][NMAT][4];
   {
-    const int k0 = kof(0);
+    const int k0 = kc(0) * kRowBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
-        *reinterpret_cast<uint4*>(&sb[wave][m][bdst[i]]) = *reinterpret_cast<const uint4*>(wsrc(m) + (size_t)4 * i * K + k0);
+        *reinterpret_cast<uint4*>(&sb[wave][m][bdst[i]]) = *reinterpret_cast<const uint4*>(wsrc(m) + 4 * i * RP + k0);
   }
 #pragma unroll
   for (int l = 0; l < LA; ++l) {
-    const int ko = kof(1 + l < NC ? 1 + l : NC - 1);
+    const int ko = kc(1 + l < NC ? 1 + l : NC - 1) * kRowBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
-        bq[l][m][i] = *reinterpret_cast<const uint4*>(wsrc(m) + (size_t)4 * i * K + ko);
+        bq[l][m][i] = *reinterpret_cast<const WRow*>(wsrc(m) + 4 * i * RP + ko);
   }
 #pragma unroll
   for (int i = 0; i < AL; ++i)
-    *reinterpret_cast<uint4*>(&sa[0][adst[i]]) = *reinterpret_cast<const uint4*>(p.a + aoff[i] + kof(0));
+    if (AFULL || tid + NTH * i < RB * ACH)
+      *reinterpret_cast<uint4*>(&sa[0][adst[i]]) = *reinterpret_cast<const uint4*>(p.a + aoff[i] + kc(0) * KC);
   __syncthreads();
 
-  for (int c = 0; c < NC; ++c) {
+  for (int c0 = 0; c0 < NC; c0 += UN) {
+#pragma unroll
+  for (int u = 0; u < UN; ++u) {
+    const int c = c0 + u;
+    if (UN > 1 && c >= NC) break;
     // the last chunk re-reads itself so loads and stores stay unconditional
-    const int ka = kof(c + 1 < NC ? c + 1 : c);
-    uint4 ra[AL];
+    const int ka = kc(c + 1 < NC ? c + 1 : c) * KC;
+    // (FP8's longer chunks need up to 8 of these per thread: kept as native
+    // vectors, which stay in registers where a uint4 array would be copied
+    // through scratch memory)
+    ARow ra[AL];
 #pragma unroll
-    for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ka);
-    const uint16_t* L = sa[c & 1];
+    for (int i = 0; i < AL; ++i)
+      if (AFULL || tid + NTH * i < RB * ACH) ra[i] = *reinterpret_cast<const ARow*>(p.a + aoff[i] + ka);
+    const uint16_t* L = sa[NABUF == 1 ? 0 : (c & 1)];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NSUB; ++s) {
       const int ch = s * 4 + (lane >> 4);
-      uint4 bf[NMAT];
+      u32x4_t bf[NMAT];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-        bf[m] = *reinterpret_cast<const uint4*>(&sb[wave][m][fr * kSK + ((ch ^ fr) << 3)]);
+      for (int m = 0; m < NMAT; ++m) bf[m] = weight_fragment<F8>(&sb[wave][m][0], s, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = i * 16 + fr;
-        const uint4 af = *reinterpret_cast<const uint4*>(&L[r * kSK + ((ch ^ (r & 15)) << 3)]);
+        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&L[r * KC + ((ch ^ (r & 15)) << 3)]);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) acc[m][i] = mfma16(af, bf[m], acc[m][i]);
       }
     }
     // chunk c+1 (oldest registers) into this wave's LDS slot, after this
-    // wave's reads of chunk c; rotate; fetch chunk c+1+LA
+    // wave's reads of chunk c; fetch chunk c+1+LA into the freed set
+    const int su = F8 ? u : 0;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sb[wave][m][bdst[i]]) = bq[0][m][i];
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<WRow*>(&sb[wave][m][bdst[i]]) = bq[su][m][i];
+    if (!F8) {
 #pragma unroll
-    for (int l = 0; l + 1 < LA; ++l)
+      for (int l = 0; l + 1 < LA; ++l)
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bq[l][m][i] = bq[l + 1][m][i];
+          for (int i = 0; i < 4; ++i) bq[l][m][i] = bq[l + 1][m][i];
+    }
     {
       const int cn = c + 1 + LA;
-      const int ko = kof(cn < NC ? cn : NC - 1);
+      const int ko = kc(cn < NC ? cn : NC - 1) * kRowBytes;
+      const int sl = F8 ? u : LA - 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
-          bq[LA - 1][m][i] = *reinterpret_cast<const uint4*>(wsrc(m) + (size_t)4 * i * K + ko);
+          bq[sl][m][i] = *reinterpret_cast<const WRow*>(wsrc(m) + 4 * i * RP + ko);
     }
+    if (NABUF == 1) __syncthreads();          // every wave is done with this chunk's token rows
 #pragma unroll
-    for (int i = 0; i < AL; ++i) *reinterpret_cast<uint4*>(&sa[(c + 1) & 1][adst[i]]) = ra[i];
+    for (int i = 0; i < AL; ++i)
+      if (AFULL || tid + NTH * i < RB * ACH)
+        *reinterpret_cast<ARow*>(&sa[NABUF == 1 ? 0 : ((c + 1) & 1)][adst[i]]) = ra[i];
     __syncthreads();
+  }
   }
 
   const int col = col0 + fr;
+  // FP8: per-output-channel scales of this lane's columns
+  float wsc[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    wsc[m] = 1.f;
+    if constexpr (F8) {
+      const size_t ch = (size_t)e * ncols + col;
+      wsc[m] = GATEUP ? (m == 0 ? p.s0[ch] : p.s1[ch]) : p.s0[ch + m * kSCols];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -208,13 +294,13 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
       if (r >= nrows) continue;
       const int orow = row0 + r;
       if (GATEUP) {
-        const float g = acc[0][i][q], u = acc[1][i][q];
+        const float g = acc[0][i][q] * wsc[0], u = acc[1][i][q] * wsc[1];
         p.out[(size_t)orow * ncols + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
       } else {
         const float sc = p.row_scale ? p.row_scale[orow] : 1.f;
         const size_t dst = (size_t)(p.out_rows ? p.out_rows[orow] : orow) * ncols + col;
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) p.out[dst + m * kSCols] = f32_to_bf16(acc[m][i][q] * sc);
+        for (int m = 0; m < NMAT; ++m) p.out[dst + m * kSCols] = f32_to_bf16(acc[m][i][q] * wsc[m] * sc);
       }
     }
   }
@@ -226,12 +312,16 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_kernel(FfnArgs p) {
 // stages its own token rows and weight rows in private LDS slots, so the k
 // loop has no block barrier; the four partial tiles are summed in wave order
 // through LDS at the end (deterministic).
-template <bool GATEUP>
+template <bool GATEUP, bool F8>
 __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
   constexpr int RB = 16;
+  constexpr int KC = F8 ? 2 * kSK : kSK;     // contraction elements per chunk
+  constexpr int ACH = KC / 8;                // 16-byte pieces of a token row per chunk
+  constexpr int AI = RB * ACH / 64;          // token-row loads per lane per chunk
+  constexpr int NSUB = KC / 32;
   constexpr int WCOLS = GATEUP ? kSCols : 2 * kSCols;   // output columns per block
   constexpr int LA = 2;
-  __shared__ __align__(16) uint16_t sa[4][RB * kSK];
+  __shared__ __align__(16) uint16_t sa[4][RB * KC];
   __shared__ __align__(16) uint16_t sb[4][2][kSCols * kSK];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tp[kMaxGroups + 1];
@@ -239,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = p.K, ncols = p.ncols;
   const int NT = ncols / WCOLS;
-  const int NC = K / kSK;                     // the host sends only K % 128 == 0 here
+  const int NC = K / KC;                      // the host sends only K % KC == 0 here
   const int c0 = (wave * NC) / 4, c1 = ((wave + 1) * NC) / 4;   // this wave's chunks
   const int total = build_tile_list<RB>(p, NT, s_off, s_tp);
   const int tile = blockIdx.x;
@@ -254,23 +344,28 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
   const int col0 = ct * WCOLS;
 
   const int brow = lane >> 4, bch = lane & 15, fr = lane & 15;
-  const size_t wrow = ((size_t)e * ncols + col0 + brow) * K + bch * 8;
-  const uint16_t* wb0 = p.w0 + wrow;
-  const uint16_t* wb1 = GATEUP ? p.w1 + wrow : p.w0 + wrow + (size_t)kSCols * K;
+  const size_t RP = (size_t)K * (F8 ? 1 : 2);                 // weight row pitch in bytes
+  const uint8_t* w0b = F8 ? p.q0 : reinterpret_cast<const uint8_t*>(p.w0);
+  const uint8_t* w1b = F8 ? p.q1 : reinterpret_cast<const uint8_t*>(p.w1);
+  const size_t wrow = ((size_t)e * ncols + col0 + brow) * RP + bch * 16;
+  const uint8_t* wb0 = w0b + wrow;
+  const uint8_t* wb1 = GATEUP ? w1b + wrow : wb0 + (size_t)kSCols * RP;
   int bdst[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * i + brow;
     bdst[i] = r * kSK + ((bch ^ r) << 3);
   }
-  // token rows: lane loads rows 4i + (lane >> 4), chunk lane & 15 (like the weights)
-  uint32_t aoff[4];
+  // token rows: load i of a lane covers row (64 / ACH) i + lane / ACH, piece lane % ACH
+  uint32_t aoff[AI];
+  int adst[AI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * i + brow;
+  for (int i = 0; i < AI; ++i) {
+    const int r = (64 / ACH) * i + lane / ACH, ch = lane % ACH;
     const int rr = (r < nrows) ? r : 0;
     const int grow = p.a_rows ? p.a_rows[row0 + rr] : (row0 + rr);
-    aoff[i] = (uint32_t)grow * (uint32_t)K + bch * 8;
+    aoff[i] = (uint32_t)grow * (uint32_t)K + ch * 8;
+    adst[i] = r * KC + ((ch ^ (r & 15)) << 3);
   }
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 
@@ -279,60 +374,68 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
     // so that concurrent blocks spread over the weight rows' offsets
     const int L = c1 - c0;
     const int rot = (int)(blockIdx.x % (unsigned)L);
-    auto kof = [c0, L, rot](int j) {
+    auto kc = [c0, L, rot](int j) {
       const int jj = j + rot;
-      return (c0 + (jj >= L ? jj - L : jj)) * kSK;
+      return c0 + (jj >= L ? jj - L : jj);
     };
     // prologue: chunk 0 of the walk into LDS, chunks 1..LA into registers
+    {
+      const int k0 = kc(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ko = kof(0);
-      *reinterpret_cast<uint4*>(&sa[wave][bdst[i]]) = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ko);
-      *reinterpret_cast<uint4*>(&sb[wave][0][bdst[i]]) = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K + ko);
-      *reinterpret_cast<uint4*>(&sb[wave][1][bdst[i]]) = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K + ko);
-    }
-    uint4 qa[LA][4], qb[LA][2][4];
-#pragma unroll
-    for (int l = 0; l < LA; ++l) {
-      const int ko = kof(min(1 + l, L - 1));
+      for (int i = 0; i < AI; ++i)
+        *reinterpret_cast<uint4*>(&sa[wave][adst[i]]) = *reinterpret_cast<const uint4*>(p.a + aoff[i] + k0 * KC);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qa[l][i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ko);
-        qb[l][0][i] = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K + ko);
-        qb[l][1][i] = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K + ko);
+        *reinterpret_cast<uint4*>(&sb[wave][0][bdst[i]]) = *reinterpret_cast<const uint4*>(wb0 + 4 * i * RP + k0 * kRowBytes);
+        *reinterpret_cast<uint4*>(&sb[wave][1][bdst[i]]) = *reinterpret_cast<const uint4*>(wb1 + 4 * i * RP + k0 * kRowBytes);
+      }
+    }
+    uint4 qa[LA][AI], qb[LA][2][4];
+#pragma unroll
+    for (int l = 0; l < LA; ++l) {
+      const int kk = kc(min(1 + l, L - 1));
+#pragma unroll
+      for (int i = 0; i < AI; ++i) qa[l][i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + kk * KC);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qb[l][0][i] = *reinterpret_cast<const uint4*>(wb0 + 4 * i * RP + kk * kRowBytes);
+        qb[l][1][i] = *reinterpret_cast<const uint4*>(wb1 + 4 * i * RP + kk * kRowBytes);
       }
     }
     for (int c = 0; c < L; ++c) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < NSUB; ++s) {
         const int ch = s * 4 + (lane >> 4);
-        const int off = fr * kSK + ((ch ^ fr) << 3);
-        const uint4 af = *reinterpret_cast<const uint4*>(&sa[wave][off]);
-        acc0 = mfma16(af, *reinterpret_cast<const uint4*>(&sb[wave][0][off]), acc0);
-        acc1 = mfma16(af, *reinterpret_cast<const uint4*>(&sb[wave][1][off]), acc1);
+        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&sa[wave][fr * KC + ((ch ^ fr) << 3)]);
+        acc0 = mfma16(af, weight_fragment<F8>(&sb[wave][0][0], s, lane), acc0);
+        acc1 = mfma16(af, weight_fragment<F8>(&sb[wave][1][0], s, lane), acc1);
       }
       // same wave: LDS operations complete in order, so the slot can be
       // overwritten right after this wave's reads
 #pragma unroll
+      for (int i = 0; i < AI; ++i) *reinterpret_cast<uint4*>(&sa[wave][adst[i]]) = qa[0][i];
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(&sa[wave][bdst[i]]) = qa[0][i];
         *reinterpret_cast<uint4*>(&sb[wave][0][bdst[i]]) = qb[0][0][i];
         *reinterpret_cast<uint4*>(&sb[wave][1][bdst[i]]) = qb[0][1][i];
       }
 #pragma unroll
-      for (int l = 0; l + 1 < LA; ++l)
+      for (int l = 0; l + 1 < LA; ++l) {
+#pragma unroll
+        for (int i = 0; i < AI; ++i) qa[l][i] = qa[l + 1][i];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          qa[l][i] = qa[l + 1][i];
           qb[l][0][i] = qb[l + 1][0][i];
           qb[l][1][i] = qb[l + 1][1][i];
         }
-      const int ko = kof(min(c + 1 + LA, L - 1));
+      }
+      const int kk = kc(min(c + 1 + LA, L - 1));
+#pragma unroll
+      for (int i = 0; i < AI; ++i) qa[LA - 1][i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + kk * KC);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qa[LA - 1][i] = *reinterpret_cast<const uint4*>(p.a + aoff[i] + ko);
-        qb[LA - 1][0][i] = *reinterpret_cast<const uint4*>(wb0 + (size_t)4 * i * K + ko);
-        qb[LA - 1][1][i] = *reinterpret_cast<const uint4*>(wb1 + (size_t)4 * i * K + ko);
+        qb[LA - 1][0][i] = *reinterpret_cast<const uint4*>(wb0 + 4 * i * RP + kk * kRowBytes);
+        qb[LA - 1][1][i] = *reinterpret_cast<const uint4*>(wb1 + 4 * i * RP + kk * kRowBytes);
       }
     }
   }
@@ -355,19 +458,25 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] += red[(w * 64 + lane) * 8 + q];
     const int col = col0 + fr;
+    float w0s = 1.f, w1s = 1.f;
+    if constexpr (F8) {
+      const size_t ch = (size_t)e * ncols + col;
+      w0s = p.s0[ch];
+      w1s = GATEUP ? p.s1[ch] : p.s0[ch + kSCols];
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = (lane >> 4) * 4 + q;
       if (r >= nrows) continue;
       const int orow = row0 + r;
       if (GATEUP) {
-        const float g = v[q], u = v[4 + q];
+        const float g = v[q] * w0s, u = v[4 + q] * w1s;
         p.out[(size_t)orow * ncols + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
       } else {
         const float sc = p.row_scale ? p.row_scale[orow] : 1.f;
         const size_t dst = (size_t)(p.out_rows ? p.out_rows[orow] : orow) * ncols + col;
-        p.out[dst] = f32_to_bf16(v[q] * sc);
-        p.out[dst + kSCols] = f32_to_bf16(v[4 + q] * sc);
+        p.out[dst] = f32_to_bf16(v[q] * w0s * sc);
+        p.out[dst + kSCols] = f32_to_bf16(v[4 + q] * w1s * sc);
       }
     }
   }
@@ -595,24 +704,32 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
 
 // ================================ launchers =================================
 
-template <int FM, bool GATEUP, int LA = 2>
-hipError_t launch_stream(const FfnArgs& a, int num_cu, hipStream_t st) {
-  (void)num_cu;
+template <int FM, bool GATEUP, bool F8, int LA = 2>
+hipError_t launch_stream(const FfnArgs& a, hipStream_t st) {
   // down: three 16-row groups per wave where the columns divide evenly and
   // two blocks still fit a CU's LDS (at most 48 rows per pass)
   const bool nm3 = !GATEUP && FM <= 3 && a.ncols % (4 * 3 * kSCols) == 0;
-  const int NT = a.ncols / (4 * kSCols * (GATEUP ? 1 : (nm3 ? 3 : 2)));
+  // FP8 gate+up: eight waves per block where the columns divide evenly
+  constexpr int NWG = (GATEUP && F8) ? 8 : 4;
+  const bool w8 = NWG == 8 && a.ncols % (8 * kSCols) == 0;
+  const int NT = a.ncols / ((w8 ? 8 : 4) * kSCols * (GATEUP ? 1 : (nm3 ? 3 : 2)));
   const long groups = a.E < a.rows_total ? a.E : a.rows_total;   // non-empty groups, at most
   const long passes = a.rows_total / (FM * 16) + groups;          // >= sum of ceil(count / rows per pass)
   const long grid = passes * NT;
   if (grid <= 0) return hipSuccess;
   if constexpr (!GATEUP && FM <= 3) {
     if (nm3) {
-      hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP, LA, 3>), dim3((unsigned)grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP, LA, 3, F8, 4>), dim3((unsigned)grid), dim3(256), 0, st, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP, LA, 2>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  if constexpr (NWG == 8) {
+    if (w8) {
+      hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP, LA, 2, F8, 8>), dim3((unsigned)grid), dim3(512), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP, LA, 2, F8, 4>), dim3((unsigned)grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -649,22 +766,26 @@ bool use_split_waves(const FfnArgs& a, bool gateup) {
   return blocks < 1024;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool F8>
 hipError_t launch_stream_ks(const FfnArgs& a, hipStream_t st) {
   const int NT = a.ncols / (GATEUP ? kSCols : 2 * kSCols);
   const long groups = a.E < a.rows_total ? a.E : a.rows_total;
   const long grid = (a.rows_total / 16 + groups) * NT;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_stream_ks_kernel<GATEUP>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((ffn_stream_ks_kernel<GATEUP, F8>), dim3((unsigned)grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 // Mean rows per group decides the kernel; the streaming kernel's pass height
-// covers ~1.5x the mean so that typical groups take one pass.
+// covers ~1.2x the mean so that typical groups take one pass.  bf16 weights
+// switch to the tile kernel above 56 mean rows; FP8 weights stay on the
+// streaming kernel at every size (64-row passes), the only kernel that reads
+// them.
 int stream_fm(const FfnArgs& a, bool gateup) {
-  if (a.K % kSK != 0 || a.ncols % (4 * kSCols * (gateup ? 1 : 2)) != 0) return 0;
+  const bool f8 = a.q0 != nullptr;
+  if (a.K % (f8 ? 2 * kSK : kSK) != 0 || a.ncols % (4 * kSCols * (gateup ? 1 : 2)) != 0) return 0;
   const double mean = (double)a.rows_total / (a.E > 0 ? a.E : 1);
-  if (mean > 56.0) return 0;
+  if (mean > 56.0 && !f8) return 0;
   const double need = mean * 1.2;
   if (need <= 16.0) return 1;
   if (need <= 32.0) return 2;
@@ -672,30 +793,33 @@ int stream_fm(const FfnArgs& a, bool gateup) {
   return 4;
 }
 
+template <bool GATEUP, bool F8>
+hipError_t launch_ffn(const FfnArgs& a, int num_cu, hipStream_t st) {
+  switch (stream_fm(a, GATEUP)) {
+    case 1:
+      return use_split_waves(a, GATEUP) ? launch_stream_ks<GATEUP, F8>(a, st) : launch_stream<1, GATEUP, F8>(a, st);
+    case 2: return launch_stream<2, GATEUP, F8>(a, st);
+    case 3: return launch_stream<3, GATEUP, F8>(a, st);
+    case 4: return launch_stream<4, GATEUP, F8>(a, st);
+    default: break;
+  }
+  if constexpr (F8) {
+    return hipErrorInvalidValue;                  // the host checks K and ncols for FP8 first
+  } else {
+    return launch_tile<GATEUP>(a, num_cu, st);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st) {
   if (a.rows_total == 0) return hipSuccess;
-  switch (stream_fm(a, true)) {
-    case 1: return use_split_waves(a, true) ? launch_stream_ks<true>(a, st) : launch_stream<1, true>(a, num_cu, st);
-    case 2: return launch_stream<2, true>(a, num_cu, st);
-    case 3: return launch_stream<3, true>(a, num_cu, st);
-    case 4: return launch_stream<4, true>(a, num_cu, st);
-    default: break;
-  }
-  return launch_tile<true>(a, num_cu, st);
+  return a.q0 ? launch_ffn<true, true>(a, num_cu, st) : launch_ffn<true, false>(a, num_cu, st);
 }
 
 hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st) {
   if (a.rows_total == 0) return hipSuccess;
-  switch (stream_fm(a, false)) {
-    case 1: return use_split_waves(a, false) ? launch_stream_ks<false>(a, st) : launch_stream<1, false>(a, num_cu, st);
-    case 2: return launch_stream<2, false>(a, num_cu, st);
-    case 3: return launch_stream<3, false>(a, num_cu, st);
-    case 4: return launch_stream<4, false>(a, num_cu, st);
-    default: break;
-  }
-  return launch_tile<false>(a, num_cu, st);
+  return a.q0 ? launch_ffn<false, true>(a, num_cu, st) : launch_ffn<false, false>(a, num_cu, st);
 }
 
 }  // namespace moe

@@ -60,9 +60,22 @@ struct FfnArgs {
   // token row of the layer output: top-1 routing without shared experts
   // needs no combine)
   const int32_t* out_rows = nullptr;
+  // FP8 weights: if q0 is set, w0/w1 are unused and q0/q1 hold OCP E4M3
+  // codes laid out like them; s0/s1 [E][ncols] are the float32 scales of
+  // each output channel (weight = value(code) * scale)
+  const uint8_t* q0 = nullptr;
+  const uint8_t* q1 = nullptr;
+  const float* s0 = nullptr;
+  const float* s1 = nullptr;
 };
 hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st);
+
+// Per-row OCP E4M3 quantisation: scale[r] = max_k |w[r][k]| / 448 (1 for a
+// zero row), q[r][k] = E4M3 nearest to w[r][k] / scale[r], ties to even,
+// saturating.  cols % 8 == 0.
+hipError_t launch_quantize_fp8(const uint16_t* w, long long rows, int cols, uint8_t* q, float* scale,
+                               hipStream_t st);
 
 struct CombineArgs {
   const uint16_t* y;         // [A][M] bf16

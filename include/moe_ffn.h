@@ -53,6 +53,7 @@ extern "C" {
 #define MOE_FFN_ABI_VERSION 1
 
 typedef uint16_t moe_bf16;   /* raw bfloat16 bits */
+typedef uint8_t moe_fp8;     /* raw OCP FP8 E4M3 bits */
 typedef void* moe_stream;    /* a hipStream_t */
 
 typedef struct moe_dims {
@@ -81,6 +82,23 @@ enum {
    * on the device (no fault; the result is that of the clamped id). */
   MOE_FLAG_IDS_IN = 1u
 };
+
+/*
+ * FP8 expert weights: OCP 8-bit floating point E4M3 codes (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent 0 = subnormals m * 2^-9;
+ * S.1111.111 = NaN; no infinity; largest finite 448) with one float32 scale
+ * per output channel: weight[e][c][j] = value(code[e][c][j]) * scale[e][c].
+ * Codes are laid out like the bf16 matrices; NaN codes must not occur (the
+ * quantiser never writes them).  All six pointers are device pointers.
+ */
+typedef struct moe_fp8_ffn {
+  const moe_fp8* gate;       /* [E][H][M] codes                                  */
+  const moe_fp8* up;         /* [E][H][M] codes                                  */
+  const moe_fp8* down;       /* [E][M][H] codes                                  */
+  const float* gate_scale;   /* [E][H]                                           */
+  const float* up_scale;     /* [E][H]                                           */
+  const float* down_scale;   /* [E][M]                                           */
+} moe_fp8_ffn;
 
 /* Stage boundaries recorded by moe_set_stage_events. */
 #define MOE_STAGE_EVENTS 7
@@ -162,6 +180,39 @@ int moe_grouped_ffn(const moe_dims* dims, const moe_bf16* x_sorted, const int32_
                     void* ws, size_t ws_bytes, moe_stream stream);
 
 /*
+ * moe_quantize_fp8 - per-output-channel FP8 quantisation of a weight matrix.
+ * The page on MoE latency, in its section on what to do about the cost, names
+ * quantising weights as a way to move fewer bytes and asks that the numerical
+ * error be measured; the format and scale rule are this library's reading:
+ *   scale[r]  = max_j |w[r][j]| / 448 in float32 (1 for an all-zero row)
+ *   q[r][j]   = the E4M3 code nearest to w[r][j] / scale[r] (float32
+ *               quotient), ties to the even code, magnitudes >= 448
+ *               saturated to 448, the sign kept (-0 for small negatives)
+ * w [rows][cols] bf16 (rows = output channels: E*H for gate/up, E*M for
+ * down; cols = the contraction); q [rows][cols] (out); scale [rows] (out).
+ * 1 <= rows <= 2^26; 64 <= cols <= 65536, cols % 64 == 0.  A one-off weight
+ * conversion, not part of the layer's path.
+ */
+int moe_quantize_fp8(const moe_bf16* w, int64_t rows, int32_t cols, moe_fp8* q, float* scale,
+                     moe_stream stream);
+
+/*
+ * moe_grouped_ffn_fp8 - moe_grouped_ffn with FP8 expert weights.  The same
+ * computation with each weight read as value(code) * scale: the codes are
+ * widened to bf16 exactly, products are summed in fp32 and the channel's
+ * scale multiplies the sum.  Every weight costs one byte of HBM traffic
+ * instead of two, which is what bounds decode-sized batches (page on MoE
+ * latency, section "router 之后还有一串动作": the grouped GEMM's cost in decode
+ * is reading weights).  experts: a host pointer to the weight set.  Needs
+ * hidden % 256 == 0 and expert_width % 256 == 0 (else MOE_ERR_UNSUPPORTED).
+ * Workspace: moe_grouped_ffn_workspace_bytes.  All batch sizes run the
+ * weight-streaming kernels (at most 64 rows per pass over the weights).
+ */
+int moe_grouped_ffn_fp8(const moe_dims* dims, const moe_bf16* x_sorted, const int32_t* expert_offsets,
+                        const moe_fp8_ffn* experts, const float* row_scale, moe_bf16* y_sorted,
+                        void* ws, size_t ws_bytes, moe_stream stream);
+
+/*
  * moe_combine - unpermute and sum.  Page on MoE latency, section
  * "router 之后还有一串动作": results go back to token order through the inverse
  * mapping, are multiplied by the routing weight and summed.
@@ -202,6 +253,20 @@ int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x,
               void* ws, size_t ws_bytes, moe_stream stream);
 
 /*
+ * moe_layer_fp8 - moe_layer with FP8 weights for the routed experts and, if
+ * n_shared > 0, the shared experts (their concatenation [S*Hs][M] and
+ * [M][S*Hs] quantised as one matrix each, one scale per output channel).
+ * The router stays bf16.  experts / shared: host pointers to the weight sets
+ * (shared NULL iff n_shared = 0).  Needs hidden, expert_width and
+ * n_shared*shared_width to be multiples of 256 (else MOE_ERR_UNSUPPORTED).
+ * Workspace: moe_layer_workspace_bytes.  Stage events as for moe_layer.
+ */
+int moe_layer_fp8(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,
+                  const float* router_bias, const moe_fp8_ffn* experts, const moe_fp8_ffn* shared,
+                  int32_t* topk_ids, float* topk_weights, moe_bf16* out, void* ws, size_t ws_bytes,
+                  moe_stream stream);
+
+/*
  * moe_set_stage_events - per-stage timing of the next moe_layer call on the
  * calling thread.  The page on MoE latency, section "最慢的 GPU 决定这一步",
  * asks for per-step records of dispatch, expert and combine times; this hook
@@ -211,7 +276,7 @@ int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x,
  *   [0] start  [1] after routing  [2] after dispatch/permutation
  *   [3] after the shared experts  [4] after the gate+up GEMM
  *   [5] after the down GEMM  [6] after the combine (end).
- * The setting is consumed by that one call.  events = NULL clears it.
+ * The setting is consumed by that one call (moe_layer or moe_layer_fp8).  events = NULL clears it.
  * n must equal MOE_STAGE_EVENTS.
  */
 int moe_set_stage_events(void* const* events, int n);

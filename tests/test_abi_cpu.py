@@ -28,7 +28,7 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_exports_every_declared_function(lib):
@@ -127,6 +127,51 @@ def test_other_entry_points_reject(lib):
     assert lib.moe_grouped_ffn(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30,
                                None) == _lib.MOE_ERR_INVALID
     assert lib.moe_combine(ctypes.byref(d), FAKE, FAKE, MIS, None, FAKE, None) == _lib.MOE_ERR_INVALID
+
+
+def _f8(**over):
+    f = dict(gate=FAKE, up=FAKE, down=FAKE, gate_scale=FAKE, up_scale=FAKE, down_scale=FAKE)
+    f.update(over)
+    return _lib.MoeFp8Ffn(**f)
+
+
+def test_fp8_entry_points_reject(lib):
+    q = lib.moe_quantize_fp8
+    assert q(FAKE, 0, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID and "rows" in _err(lib)
+    assert q(FAKE, 4, 100, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID and "cols" in _err(lib)
+    assert q(None, 4, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID and "w is NULL" in _err(lib)
+    assert q(FAKE, 4, 128, MIS, FAKE, None) == _lib.MOE_ERR_INVALID and "aligned" in _err(lib)
+    assert q(FAKE, 4, 128, FAKE, None, None) == _lib.MOE_ERR_INVALID and "scale" in _err(lib)
+
+    g = lib.moe_grouped_ffn_fp8
+    d = D(M=256, H=256)
+    ok = _f8()
+    assert g(ctypes.byref(D(M=192, H=256)), FAKE, FAKE, ctypes.byref(ok), None, FAKE, FAKE, 1 << 30,
+             None) == _lib.MOE_ERR_UNSUPPORTED and "hidden" in _err(lib)
+    assert g(ctypes.byref(D(M=256, H=192)), FAKE, FAKE, ctypes.byref(ok), None, FAKE, FAKE, 1 << 30,
+             None) == _lib.MOE_ERR_UNSUPPORTED and "expert_width" in _err(lib)
+    assert g(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, FAKE, 1 << 30, None) == _lib.MOE_ERR_INVALID
+    assert "experts is NULL" in _err(lib)
+    bad = _f8(down_scale=None)
+    assert g(ctypes.byref(d), FAKE, FAKE, ctypes.byref(bad), None, FAKE, FAKE, 1 << 30,
+             None) == _lib.MOE_ERR_INVALID and "experts->down_scale" in _err(lib)
+    bad = _f8(up=MIS)
+    assert g(ctypes.byref(d), FAKE, FAKE, ctypes.byref(bad), None, FAKE, FAKE, 1 << 30,
+             None) == _lib.MOE_ERR_INVALID and "experts->up" in _err(lib)
+    assert g(ctypes.byref(d), FAKE, FAKE, ctypes.byref(ok), None, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
+
+    L = lib.moe_layer_fp8
+
+    def layer(dd, shared=None, flags=0, ws_bytes=1 << 40):
+        return L(ctypes.byref(dd), flags, FAKE, FAKE, None, ctypes.byref(ok),
+                 None if shared is None else ctypes.byref(shared), None, None, FAKE, FAKE, ws_bytes, None)
+
+    assert layer(d, shared=ok) == _lib.MOE_ERR_INVALID and "n_shared" in _err(lib)
+    ds = D(M=256, H=256, S=2, Hs=128)
+    assert layer(ds) == _lib.MOE_ERR_INVALID and "shared is NULL" in _err(lib)
+    assert layer(D(M=256, H=256, S=1, Hs=64), shared=ok) == _lib.MOE_ERR_UNSUPPORTED
+    assert layer(d, flags=4) == _lib.MOE_ERR_INVALID and "flags" in _err(lib)
+    assert layer(d, ws_bytes=16) == _lib.MOE_ERR_WORKSPACE
 
 
 def test_workspace_sizes(lib):

@@ -206,6 +206,15 @@ def _mut_scale_447(w_bits):
     return F.e4m3_encode((w / scale[..., None]).astype(np.float32)), scale
 
 
+def _mut_row_block_mixup(w_bits):
+    """One scale per block of rows instead of per row."""
+    q, s = ORIG["quantize_rows"](w_bits)
+    w = (np.asarray(w_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    amax = np.abs(w).max()
+    s = np.full_like(s, amax / np.float32(448) if amax > 0 else 1)
+    return F.e4m3_encode((w / s[..., None]).astype(np.float32)), s
+
+
 def _mut_drop_sign(v):
     return ORIG["e4m3_encode"](np.abs(np.asarray(v, dtype=np.float32)))
 
@@ -216,6 +225,7 @@ MUTANTS = [
     ("e4m3_encode", _mut_drop_sign),
     ("e4m3_value", _mut_bias8),
     ("quantize_rows", _mut_scale_447),
+    ("quantize_rows", _mut_row_block_mixup),
 ]
 
 
