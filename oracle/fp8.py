@@ -25,11 +25,20 @@ Pinned by tests/test_oracle_fp8.py against torch's float8_e4m3fn conversion
 (a library routine), a brute-force nearest-value search over all 256 codes,
 the format's own bounds, and a layer whose weights are exactly representable.
 """
+import concurrent.futures as cf
+import os
 from typing import Tuple
 
 import numpy as np
 
 E4M3_MAX = 448.0
+
+
+def _threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return max(1, min(16, os.cpu_count() or 1))
 
 
 def e4m3_value(code: int) -> float:
@@ -80,17 +89,38 @@ def e4m3_decode(code: np.ndarray) -> np.ndarray:
 
 def quantize_rows(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Per-output-channel quantisation of bf16 weights [..., K] (uint16 bits).
-    Returns codes (uint8, same shape) and scales (float32, shape[:-1])."""
-    w = (np.asarray(w_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
-    amax = np.abs(w).max(axis=-1)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    q = e4m3_encode((w / scale[..., None]).astype(np.float32))
-    return q, scale
+    Returns codes (uint8, same shape) and scales (float32, shape[:-1]).
+    Rows are independent; they are taken in blocks of about 2^20 weights, on
+    a few threads, only to keep the temporaries small and the wait short."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    K = w_bits.shape[-1]
+    flat = w_bits.reshape(-1, K)
+    q = np.empty(flat.shape, np.uint8)
+    scale = np.empty(flat.shape[0], np.float32)
+    step = max(1, (1 << 20) // K)
+
+    def block(r0):
+        w = (flat[r0:r0 + step].astype(np.uint32) << np.uint32(16)).view(np.float32)
+        amax = np.abs(w).max(axis=-1)
+        s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        q[r0:r0 + step] = e4m3_encode((w / s[:, None]).astype(np.float32))
+        scale[r0:r0 + step] = s
+
+    starts = range(0, flat.shape[0], step)
+    if len(starts) > 1:
+        with cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(block, starts))
+    else:
+        for r0 in starts:
+            block(r0)
+    return q.reshape(w_bits.shape), scale.reshape(w_bits.shape[:-1])
 
 
 def dequantize_rows(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """value(code) * scale, float64."""
-    return e4m3_decode(q) * np.asarray(scale, np.float64)[..., None]
+    out = e4m3_decode(q)
+    out *= np.asarray(scale, np.float64)[..., None]
+    return out
 
 
 class DequantizedExperts:
