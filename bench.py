@@ -2,6 +2,7 @@
 """Throughput of one MoE FFN layer (moe_layer) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--tokens N]
+                    [--fp8 | --micro-batches M | --cost-model]
 
 A step is one moe_layer call over one batch of synthetic, seeded input that is
 already resident in HBM: router -> top-k -> dispatch/permutation -> grouped
@@ -169,6 +170,9 @@ def main() -> int:
                     help="run moe_layer_fp8: expert weights quantised once (moe_quantize_fp8, OCP E4M3 "
                          "with per-channel scales) before timing; activations and h stay bf16; no CPU "
                          "baseline in this mode")
+    ap.add_argument("--micro-batches", type=int, default=1,
+                    help="run moe_layer_pipelined with this many micro-batches overlapped on two streams "
+                         "(per-stage events are not available in this mode; the roofline is the layer's)")
     ap.add_argument("--cost-model", action="store_true",
                     help="instead of the layer: time one expert's SwiGLU FFN over per-expert batches "
                          "1..4096 at each workload's (M, H) and fit t(m) = alpha + beta*m (one JSON "
@@ -218,7 +222,19 @@ def main() -> int:
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
+    pipelined = args.micro_batches > 1
+    if pipelined:
+        if args.fp8:
+            raise SystemExit("bench.py: --micro-batches runs the bf16 layer only")
+        ws = moe.workspace(moe.moe_layer_pipelined_workspace_bytes(dm, args.micro_batches, flags), dev)
+
     def step(events=None):
+        if pipelined:
+            moe.moe_layer_pipelined(dm, args.micro_batches, T["x"], T["w_gate"], T["w_up"], T["w_down"],
+                                    w_router=T.get("w_router"), router_bias=T.get("router_bias"),
+                                    ws_gate=T.get("ws_gate"), ws_up=T.get("ws_up"), ws_down=T.get("ws_down"),
+                                    topk_ids=ids, topk_weights=wts, ids_in=w.pre_routed, out=out, ws=ws)
+            return
         if events is not None:
             moe.moe_set_stage_events(events)
         if args.fp8:
@@ -250,11 +266,18 @@ def main() -> int:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     # instrumented steps (stage events inside the layer): per-stage times and,
-    # with --flush, the layer time between its first and last event
+    # with --flush, the layer time between its first and last event; the
+    # micro-batched layer records its whole call between two events instead
     for i in range(K):
         if flush_buf is not None:
             flush_buf.fill_(i & 0xff)
-        step(evs[i])
+        if pipelined:
+            evs[i][0].record()
+            step()
+            for e in evs[i][1:]:
+                e.record()
+        else:
+            step(evs[i])
     torch.cuda.synchronize()
 
     stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(6)] for i in range(K)])
@@ -268,12 +291,15 @@ def main() -> int:
     F, B = layer_work(w, active, args.fp8)
     Fg, Bg = gateup_work(w, active, args.fp8)
     t_gu = stage_ms[:, 3].mean() * 1e-3
+    t_layer = ms_per_step * 1e-3
+    if pipelined:
+        # the launches of several micro-batches interleave: report the layer
+        Fg, Bg, t_gu = F, B, t_layer
     # the gate+up launch is bound by MFMA when its flops per algorithmic
     # byte exceed the ridge point (peak flops / peak bandwidth), else by HBM
     mfma_bound = Fg / Bg > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     achieved = Fg / t_gu / 1e12 if mfma_bound else Bg / t_gu / 1e9
     peak = BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS
-    t_layer = ms_per_step * 1e-3
     t_roof = max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9))
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -281,11 +307,13 @@ def main() -> int:
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.title, "N": w.N, "M": w.M, "E": w.E, "k": w.k, "H": w.H, "S": w.S, "Hs": w.Hs,
                    "expert_weights": "fp8 e4m3, per-channel fp32 scales" if args.fp8 else "bf16",
+                   "micro_batches": args.micro_batches,
                    "parallelism": "single GPU", "timing": "event-timed, caches flushed" if args.flush
                    else "wall clock over back-to-back steps"},
         "roofline": {"bound": "mfma" if mfma_bound else "hbm",
-                     "kernel": "grouped SwiGLU gate+up GEMM (ffn_stream_kernel at decode-sized experts, "
-                               "ffn_tile_kernel otherwise)",
+                     "kernel": ("whole layer, micro-batched" if pipelined else
+                                "grouped SwiGLU gate+up GEMM (ffn_stream_kernel at decode-sized experts, "
+                                "ffn_tile_kernel otherwise)"),
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s" if mfma_bound else "GB/s",
                      "frac": achieved / peak, "traffic": None, "algorithmic_bytes": Bg, "algorithmic_flops": Fg,
                      "avg_us": t_gu * 1e6},
@@ -295,7 +323,7 @@ def main() -> int:
                   "event_layer_us": float(layer_ms.mean() * 1e3),
                   # per-call spread from the instrumented pass (includes the stage events)
                   "event_layer_us_p10_p50_p90": [float(np.percentile(layer_ms, q) * 1e3) for q in (10, 50, 90)]},
-        "stages_us": {s: float(stage_ms[:, j].mean() * 1e3) for j, s in enumerate(STAGES)},
+        "stages_us": None if pipelined else {s: float(stage_ms[:, j].mean() * 1e3) for j, s in enumerate(STAGES)},
         "routing": {"active_experts": active, "max_rows": int(counts.max()), "mean_rows": float(counts.mean()),
                     "empty_experts": int((counts == 0).sum())},
     }
@@ -314,7 +342,7 @@ def main() -> int:
         torch.cuda.synchronize()
         res["copy_gbs"] = 2.0 * n * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
         del src, dst
-    tr = profiling.read_traffic(os.path.join(ROOT, "profiles",
+    tr = None if pipelined else profiling.read_traffic(os.path.join(ROOT, "profiles",
                                              f"traffic_{w.name}_N{w.N}{'_fp8' if args.fp8 else ''}.txt"))
     if tr is not None:
         res["roofline"]["traffic"] = float(tr["traffic_bytes"])

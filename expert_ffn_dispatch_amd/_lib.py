@@ -20,6 +20,7 @@ EXPORTS = (
     "moe_permute_workspace_bytes",
     "moe_grouped_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
     "moe_layer", "moe_set_stage_events", "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_layer_fp8",
+    "moe_layer_pipelined_workspace_bytes", "moe_layer_pipelined",
 )
 MOE_STAGE_EVENTS = 7
 
@@ -69,6 +70,9 @@ def load() -> ctypes.CDLL:
     lib.moe_quantize_fp8.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, P]
     lib.moe_grouped_ffn_fp8.argtypes = [DIMS, P, P, F8, P, P, P, ctypes.c_size_t, P]
     lib.moe_layer_fp8.argtypes = [DIMS, ctypes.c_uint32, P, P, P, F8, F8, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_layer_pipelined_workspace_bytes.argtypes = [DIMS, ctypes.c_uint32, ctypes.c_int32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_layer_pipelined.argtypes = [DIMS, ctypes.c_uint32, ctypes.c_int32] + [P] * 13 + [ctypes.c_size_t, P]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib

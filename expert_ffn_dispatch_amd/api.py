@@ -219,6 +219,30 @@ def moe_layer_fp8(d: MoeDims, x, experts: Fp8Weights, shared: Optional[Fp8Weight
     return out
 
 
+def moe_layer_pipelined_workspace_bytes(d: MoeDims, n_micro: int, flags: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().moe_layer_pipelined_workspace_bytes(ctypes.byref(d), flags, n_micro, ctypes.byref(n)))
+    return n.value
+
+
+def moe_layer_pipelined(d: MoeDims, n_micro: int, x, w_gate, w_up, w_down, w_router=None, router_bias=None,
+                        ws_gate=None, ws_up=None, ws_down=None, topk_ids=None, topk_weights=None,
+                        ids_in: bool = False, out=None, ws=None, stream=None):
+    dev = x.device
+    flags = MOE_FLAG_IDS_IN if ids_in else 0
+    if out is None:
+        out = torch.empty((d.n_tokens, d.hidden), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(moe_layer_pipelined_workspace_bytes(d, n_micro, flags), dev)
+    _lib.check(_lib.load().moe_layer_pipelined(
+        ctypes.byref(d), flags, n_micro, _ptr(x, _BF16_LIKE), _ptr(w_router, _BF16_LIKE),
+        _ptr(router_bias, (torch.float32,)), _ptr(w_gate, _BF16_LIKE), _ptr(w_up, _BF16_LIKE),
+        _ptr(w_down, _BF16_LIKE), _ptr(ws_gate, _BF16_LIKE), _ptr(ws_up, _BF16_LIKE),
+        _ptr(ws_down, _BF16_LIKE), _ptr(topk_ids, (torch.int32,)), _ptr(topk_weights, (torch.float32,)),
+        _ptr(out, _BF16_LIKE), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
 def moe_set_stage_events(events) -> None:
     """Record the given MOE_STAGE_EVENTS torch.cuda.Event objects at the stage
     boundaries of the next moe_layer call on this thread (None clears).  The

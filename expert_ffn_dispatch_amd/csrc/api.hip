@@ -273,11 +273,11 @@ int run_grouped_ffn(const char* fn, const moe_dims* dims, const moe_bf16* x_sort
   return ok();
 }
 
-// The whole layer; the weight pointers have been checked by the caller.
-int run_layer(const char* fn, const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,
-              const float* router_bias, const ExpertWeights& routed, const ExpertWeights& shared,
-              int32_t* topk_ids, float* topk_weights, moe_bf16* out, void* ws, size_t ws_bytes,
-              moe_stream stream) {
+// Argument rules of the layer entry points other than the weights (checked
+// by each caller) and the workspace.
+int check_layer_args(const char* fn, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,
+                     const float* router_bias, const int32_t* topk_ids, const float* topk_weights,
+                     const moe_bf16* out) {
   if (flags & ~uint32_t(MOE_FLAG_IDS_IN)) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
   const bool ids_in = (flags & MOE_FLAG_IDS_IN) != 0;
   REQ_PTR(x);
@@ -293,21 +293,30 @@ int run_layer(const char* fn, const moe_dims* dims, uint32_t flags, const moe_bf
     OPT_PTR(topk_weights);
   }
   REQ_PTR(out);
-  Carver sz(nullptr);
-  carve_layer(sz, *dims);
-  if (int r = check_ws(fn, ws, ws_bytes, sz.off)) return r;
-  const int ncu = num_cus();
-  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
+  return MOE_OK;
+}
 
+// Optional cross-stream ordering of a layer's expert GEMMs (shared and
+// routed): wait for `before` ahead of the first, record `after` behind the
+// last.  Used by the micro-batched layer so that one micro-batch's GEMMs run
+// at a time while the small kernels around them overlap.
+struct GemmOrder {
+  hipEvent_t before = nullptr;
+  hipEvent_t after = nullptr;
+};
+
+// Enqueue the whole layer on `st`; every argument has been checked and `ws`
+// holds carve_layer(dims).  `rec`: record the stage events.
+int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_bf16* x, const moe_bf16* w_router,
+                  const float* router_bias, const ExpertWeights& routed, const ExpertWeights& shared,
+                  int32_t* topk_ids, float* topk_weights, moe_bf16* out, void* ws, hipStream_t st, int ncu,
+                  bool rec, const GemmOrder& order) {
   Carver c(ws);
   LayerWs w = carve_layer(c, *dims);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   const int N = dims->n_tokens, M = dims->hidden, E = dims->n_experts, k = dims->top_k, H = dims->expert_width;
   const int A = N * k;
   int32_t* ids = topk_ids ? topk_ids : w.ids;
   float* wts = topk_weights ? topk_weights : w.wts;
-  const bool rec = g_stage_on;
-  g_stage_on = false;
   auto mark = [&](int i) -> hipError_t { return rec ? hipEventRecord(g_stage_ev[i], st) : hipSuccess; };
   if (hipError_t e = mark(0)) return device_error(fn, e);
 
@@ -320,6 +329,9 @@ int run_layer(const char* fn, const moe_dims* dims, uint32_t flags, const moe_bf
                      w.perm.tile_hist, w.perm.tile_off};
   if (hipError_t e = moe::launch_permute(p, st)) return device_error(fn, e);
   if (hipError_t e = mark(2)) return device_error(fn, e);
+  if (order.before != nullptr) {
+    if (hipError_t e = hipStreamWaitEvent(st, order.before, 0)) return device_error(fn, e);
+  }
 
   if (dims->n_shared > 0) {
     const int SH = dims->n_shared * dims->shared_width;
@@ -369,6 +381,9 @@ int run_layer(const char* fn, const moe_dims* dims, uint32_t flags, const moe_bf
   dn.ncols = M;
   dn.out_rows = direct ? w.row_token : nullptr;
   if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  if (order.after != nullptr) {
+    if (hipError_t e = hipEventRecord(order.after, st)) return device_error(fn, e);
+  }
   if (hipError_t e = mark(5)) return device_error(fn, e);
 
   if (!direct) {
@@ -376,6 +391,119 @@ int run_layer(const char* fn, const moe_dims* dims, uint32_t flags, const moe_bf
     if (hipError_t e = moe::launch_combine(cb, st)) return device_error(fn, e);
   }
   if (hipError_t e = mark(6)) return device_error(fn, e);
+  return ok();
+}
+
+// The whole layer; the weight pointers have been checked by the caller.
+int run_layer(const char* fn, const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,
+              const float* router_bias, const ExpertWeights& routed, const ExpertWeights& shared,
+              int32_t* topk_ids, float* topk_weights, moe_bf16* out, void* ws, size_t ws_bytes,
+              moe_stream stream) {
+  if (int r = check_layer_args(fn, flags, x, w_router, router_bias, topk_ids, topk_weights, out)) return r;
+  Carver sz(nullptr);
+  carve_layer(sz, *dims);
+  if (int r = check_ws(fn, ws, ws_bytes, sz.off)) return r;
+  const int ncu = num_cus();
+  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
+  const bool rec = g_stage_on;
+  g_stage_on = false;
+  return enqueue_layer(fn, dims, (flags & MOE_FLAG_IDS_IN) != 0, x, w_router, router_bias, routed, shared,
+                       topk_ids, topk_weights, out, ws, static_cast<hipStream_t>(stream), ncu, rec, GemmOrder{});
+}
+
+// ---------------------------------------------------------------------------
+// Micro-batched layer: a second stream per calling thread and device, held
+// until the process ends (created on first use, default priority), and the
+// events that order work across the two streams.
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxMicro = 64;
+
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;       // caller's stream -> side stream
+  hipEvent_t join = nullptr;       // side stream -> caller's stream
+  hipEvent_t gemm[2] = {nullptr, nullptr};   // end of a micro-batch's GEMMs, per stream
+};
+thread_local SideStream g_side[kMaxDevices];
+
+int side_stream(const char* fn, SideStream** out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return device_error(fn, e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  SideStream& s = g_side[dev];
+  if (s.stream == nullptr) {
+    SideStream n;
+    if (hipError_t e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking)) return device_error(fn, e);
+    hipEvent_t* evs[4] = {&n.fork, &n.join, &n.gemm[0], &n.gemm[1]};
+    for (hipEvent_t* ev : evs)
+      if (hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) return device_error(fn, e);
+    s = n;
+  }
+  *out = &s;
+  return MOE_OK;
+}
+
+// Token range of micro-batch i of n over N tokens (sizes differ by at most one).
+void micro_range(int N, int n, int i, int* start, int* count) {
+  const int base = N / n, extra = N % n;
+  *start = i * base + (i < extra ? i : extra);
+  *count = base + (i < extra ? 1 : 0);
+}
+
+moe_dims micro_dims(const moe_dims& d, int n_micro) {
+  moe_dims m = d;
+  m.n_tokens = (d.n_tokens + n_micro - 1) / n_micro;
+  return m;
+}
+
+size_t pipelined_ws_bytes(const moe_dims& d, int n_micro) {
+  const moe_dims m = micro_dims(d, n_micro);
+  Carver c(nullptr);
+  carve_layer(c, m);
+  return n_micro > 1 ? 2 * c.off : c.off;
+}
+
+int run_layer_pipelined(const char* fn, const moe_dims* dims, uint32_t flags, int32_t n_micro, const moe_bf16* x,
+                        const moe_bf16* w_router, const float* router_bias, const ExpertWeights& routed,
+                        const ExpertWeights& shared, int32_t* topk_ids, float* topk_weights, moe_bf16* out,
+                        void* ws, size_t ws_bytes, moe_stream stream) {
+  if (n_micro < 1 || n_micro > kMaxMicro || n_micro > dims->n_tokens)
+    return fail(MOE_ERR_INVALID, "%s: n_micro=%d must be in [1, min(%d, n_tokens)]", fn, n_micro, kMaxMicro);
+  if (int r = check_layer_args(fn, flags, x, w_router, router_bias, topk_ids, topk_weights, out)) return r;
+  if (int r = check_ws(fn, ws, ws_bytes, pipelined_ws_bytes(*dims, n_micro))) return r;
+  const int ncu = num_cus();
+  if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
+  g_stage_on = false;
+  const bool ids_in = (flags & MOE_FLAG_IDS_IN) != 0;
+  hipStream_t main_st = static_cast<hipStream_t>(stream);
+  if (n_micro == 1)
+    return enqueue_layer(fn, dims, ids_in, x, w_router, router_bias, routed, shared, topk_ids, topk_weights, out,
+                         ws, main_st, ncu, false, GemmOrder{});
+  SideStream* side = nullptr;
+  if (int r = side_stream(fn, &side)) return r;
+  const size_t slot = pipelined_ws_bytes(*dims, n_micro) / 2;
+  const int M = dims->hidden, k = dims->top_k;
+  if (hipError_t e = hipEventRecord(side->fork, main_st)) return device_error(fn, e);
+  if (hipError_t e = hipStreamWaitEvent(side->stream, side->fork, 0)) return device_error(fn, e);
+  for (int i = 0; i < n_micro; ++i) {
+    int t0 = 0, nt = 0;
+    micro_range(dims->n_tokens, n_micro, i, &t0, &nt);
+    moe_dims d = *dims;
+    d.n_tokens = nt;
+    hipStream_t st = (i & 1) ? side->stream : main_st;
+    GemmOrder order;
+    order.before = i > 0 ? side->gemm[(i - 1) & 1] : nullptr;
+    order.after = side->gemm[i & 1];
+    void* wsi = static_cast<char*>(ws) + (i & 1) * slot;
+    if (int r = enqueue_layer(fn, &d, ids_in, x + (size_t)t0 * M, w_router, router_bias, routed, shared,
+                              topk_ids ? topk_ids + (size_t)t0 * k : nullptr,
+                              topk_weights ? topk_weights + (size_t)t0 * k : nullptr, out + (size_t)t0 * M, wsi,
+                              st, ncu, false, order))
+      return r;
+  }
+  if (hipError_t e = hipEventRecord(side->join, side->stream)) return device_error(fn, e);
+  if (hipError_t e = hipStreamWaitEvent(main_st, side->join, 0)) return device_error(fn, e);
   return ok();
 }
 
@@ -590,6 +718,39 @@ int moe_layer_fp8(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const
   }
   return run_layer(fn, dims, flags, x, w_router, router_bias, fp8_weights(experts), fp8_weights(shared),
                    topk_ids, topk_weights, out, ws, ws_bytes, stream);
+}
+
+int moe_layer_pipelined_workspace_bytes(const moe_dims* dims, uint32_t flags, int32_t n_micro, size_t* bytes) {
+  const char* fn = "moe_layer_pipelined_workspace_bytes";
+  if (int r = check_dims(fn, dims, true)) return r;
+  if (flags & ~uint32_t(MOE_FLAG_IDS_IN)) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+  if (n_micro < 1 || n_micro > kMaxMicro || n_micro > dims->n_tokens)
+    return fail(MOE_ERR_INVALID, "%s: n_micro=%d must be in [1, min(%d, n_tokens)]", fn, n_micro, kMaxMicro);
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID, "%s: bytes is NULL", fn);
+  *bytes = pipelined_ws_bytes(*dims, n_micro);
+  return ok();
+}
+
+int moe_layer_pipelined(const moe_dims* dims, uint32_t flags, int32_t n_micro, const moe_bf16* x,
+                        const moe_bf16* w_router, const float* router_bias, const moe_bf16* w_gate,
+                        const moe_bf16* w_up, const moe_bf16* w_down, const moe_bf16* ws_gate,
+                        const moe_bf16* ws_up, const moe_bf16* ws_down, int32_t* topk_ids, float* topk_weights,
+                        moe_bf16* out, void* ws, size_t ws_bytes, moe_stream stream) {
+  const char* fn = "moe_layer_pipelined";
+  if (int r = check_dims(fn, dims, true)) return r;
+  REQ_PTR(w_gate);
+  REQ_PTR(w_up);
+  REQ_PTR(w_down);
+  if (dims->n_shared > 0) {
+    REQ_PTR(ws_gate);
+    REQ_PTR(ws_up);
+    REQ_PTR(ws_down);
+  } else if (ws_gate || ws_up || ws_down) {
+    return fail(MOE_ERR_INVALID, "%s: shared-expert weights given with n_shared = 0", fn);
+  }
+  return run_layer_pipelined(fn, dims, flags, n_micro, x, w_router, router_bias, bf16_weights(w_gate, w_up, w_down),
+                             bf16_weights(ws_gate, ws_up, ws_down), topk_ids, topk_weights, out, ws, ws_bytes,
+                             stream);
 }
 
 }  // extern "C"

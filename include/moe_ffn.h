@@ -267,6 +267,30 @@ int moe_layer_fp8(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const
                   moe_stream stream);
 
 /*
+ * moe_layer_pipelined - moe_layer over n_micro micro-batches of consecutive
+ * tokens (sizes differ by at most one), overlapped on two streams: the
+ * single-GPU form of the ping-pong pipeline of the MegaScale-Infer summary
+ * (核心贡献 2: m micro-batches keep the attention and expert stages busy at the
+ * same time).  Micro-batches alternate between `stream` and a second stream
+ * that the library creates on first use per calling thread and device (default
+ * priority, held until the process ends); the expert GEMMs of micro-batch i
+ * start after those of micro-batch i-1 end, while routing, permutation and
+ * combine of the neighbouring micro-batches run beside them.  The call
+ * returns with all work ordered before later work on `stream`.  Each token's
+ * result equals moe_layer's up to the summation order of its expert GEMMs
+ * (the kernels are chosen per micro-batch size).  Arguments as for moe_layer;
+ * 1 <= n_micro <= min(64, n_tokens); n_micro = 1 is moe_layer on `stream`.
+ * Workspace: moe_layer_pipelined_workspace_bytes (two micro-batch slots).
+ * Stage events are not recorded (a pending moe_set_stage_events is dropped).
+ */
+int moe_layer_pipelined_workspace_bytes(const moe_dims* dims, uint32_t flags, int32_t n_micro, size_t* bytes);
+int moe_layer_pipelined(const moe_dims* dims, uint32_t flags, int32_t n_micro, const moe_bf16* x,
+                        const moe_bf16* w_router, const float* router_bias, const moe_bf16* w_gate,
+                        const moe_bf16* w_up, const moe_bf16* w_down, const moe_bf16* ws_gate,
+                        const moe_bf16* ws_up, const moe_bf16* ws_down, int32_t* topk_ids, float* topk_weights,
+                        moe_bf16* out, void* ws, size_t ws_bytes, moe_stream stream);
+
+/*
  * moe_set_stage_events - per-stage timing of the next moe_layer call on the
  * calling thread.  The page on MoE latency, section "最慢的 GPU 决定这一步",
  * asks for per-step records of dispatch, expert and combine times; this hook

@@ -174,6 +174,32 @@ def test_fp8_entry_points_reject(lib):
     assert layer(d, ws_bytes=16) == _lib.MOE_ERR_WORKSPACE
 
 
+def test_pipelined_rejects(lib):
+    d = D(N=8)
+    n = ctypes.c_size_t(0)
+
+    def call(dd, n_micro, flags=0, ws_bytes=1 << 40, **over):
+        a = dict(x=FAKE, w_router=FAKE, w_gate=FAKE, w_up=FAKE, w_down=FAKE, out=FAKE)
+        a.update(over)
+        return lib.moe_layer_pipelined(ctypes.byref(dd), flags, n_micro, a["x"], a["w_router"], None, a["w_gate"],
+                                       a["w_up"], a["w_down"], None, None, None, None, None, a["out"], FAKE,
+                                       ws_bytes, None)
+
+    assert call(d, 0) == _lib.MOE_ERR_INVALID and "n_micro" in _err(lib)
+    assert call(d, 9) == _lib.MOE_ERR_INVALID and "n_micro" in _err(lib)
+    assert call(D(N=100), 65) == _lib.MOE_ERR_INVALID
+    assert call(d, 2, w_gate=None) == _lib.MOE_ERR_INVALID and "w_gate" in _err(lib)
+    assert call(d, 2, flags=1) == _lib.MOE_ERR_INVALID and "w_router" in _err(lib)
+    assert call(d, 2, ws_bytes=16) == _lib.MOE_ERR_WORKSPACE
+    r = lib.moe_layer_pipelined_workspace_bytes(ctypes.byref(d), 0, 0, ctypes.byref(n))
+    assert r == _lib.MOE_ERR_INVALID
+    # two slots of the larger micro-batch's layer workspace
+    big = moe.moe_layer_pipelined_workspace_bytes(D(N=1000), 4)
+    one = moe.moe_layer_workspace_bytes(D(N=250))
+    assert big == 2 * one
+    assert moe.moe_layer_pipelined_workspace_bytes(D(N=1000), 1) == moe.moe_layer_workspace_bytes(D(N=1000))
+
+
 def test_workspace_sizes(lib):
     def ws(d):
         return moe.moe_layer_workspace_bytes(d)
