@@ -526,6 +526,9 @@ __device__ __forceinline__ int tsw(int row) { return ((row >> 1) ^ ((row & 1) <<
 __device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
+__device__ __forceinline__ void dma16(const uint8_t* g, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
 
 // s_waitcnt for vector-memory count N only (expcnt and lgkmcnt left at their maxima)
 #define MOE_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | 0x0F70)
@@ -536,14 +539,21 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
 
 // BM token rows per tile (256, 192 or 128): each wave covers BM/2 rows,
 // FMW = BM/64 blocks of 32.
-template <bool GATEUP, int BM>
+// F8: FP8 (E4M3) weights.  A stage then holds 64 bytes of every weight row
+// (four 16-byte pieces, piece c of row r at c ^ ((r >> 2) & 3)); each lane
+// reads its eight codes of a B fragment and widens them to bf16 exactly, and
+// the per-channel scales multiply the sums in the epilogue.
+template <bool GATEUP, int BM, bool F8>
 __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
   constexpr int FMW = BM / 64;                   // 32-row MFMA blocks per wave
   constexpr int AI = BM / 64;                    // direct loads of token rows per wave per stage
+  constexpr int BI = F8 ? 2 : 4;                 // direct loads of weight rows per wave per stage
   constexpr int STA = BM * kTBK;                 // bf16 elements of the token-row part
-  __shared__ __align__(16) uint16_t sr0[(BM + kTN) * kTBK];
-  __shared__ __align__(16) uint16_t sr1[(BM + kTN) * kTBK];
+  constexpr int WRB = F8 ? kTBK : 2 * kTBK;      // bytes of a weight row per stage
+  constexpr int STG = STA + kTN * WRB / 2;       // 16-bit elements per stage
+  __shared__ __align__(16) uint16_t sr0[STG];
+  __shared__ __align__(16) uint16_t sr1[STG];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tp[kMaxGroups + 1];
 
@@ -558,20 +568,24 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
   const int fr = lane & 31, fg = lane >> 5;
 
   const int swf = tsw(fr);
+  // boff0: 16-bit elements (bf16 weights) or bytes (FP8 codes) from the stage start
   int aoff0[4], boff0[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     aoff0[s] = (wm * (BM / 2) + fr) * kTBK + (((2 * s + fg) ^ swf) << 3);
-    boff0[s] = STA + fr * kTBK + (((2 * s + fg) ^ swf) << 3);
+    boff0[s] = F8 ? 2 * STA + fr * WRB + ((s ^ ((fr >> 2) & 3)) << 4) + (fg << 3)
+                  : STA + fr * kTBK + (((2 * s + fg) ^ swf) << 3);
   }
   int brow0[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) brow0[j] = GATEUP ? (j == 0 ? wn * 32 : HC + wn * 32) : wn * 64 + 32 * j;
 
   // direct LDS loads: instruction i of this wave fills token rows
-  // (BM/8)*wave + 8*i + (lane >> 3) and weight rows 32*wave + 8*i + (lane >> 3),
-  // slot lane & 7
+  // (BM/8)*wave + 8*i + (lane >> 3), slot lane & 7, and weight rows
+  // 32*wave + 8*i + (lane >> 3), slot lane & 7 (FP8: 32*wave + 16*i + (lane >> 2),
+  // slot lane & 3)
   const int lrow = lane >> 3, lslot = lane & 7;
+  const int qrow = lane >> 2, qslot = lane & 3;
 
   for (int round = 0; round * G < total; ++round) {
     const int tile = round * G + slot;
@@ -584,11 +598,14 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     const int row0 = s_off[e] + rt * BM;
     const int nrows = min(BM, cnt - rt * BM);
     const int col0 = ct * HC;
-    const uint16_t* wexp0 = p.w0 + (size_t)e * ncols * K;
-    const uint16_t* wexp1 = GATEUP ? p.w1 + (size_t)e * ncols * K : wexp0;
+    // weight rows as bytes (bf16: 2 per element, FP8: 1)
+    constexpr int WB = F8 ? 1 : 2;
+    const uint8_t* wexp0 = (F8 ? p.q0 : reinterpret_cast<const uint8_t*>(p.w0)) + (size_t)e * ncols * K * WB;
+    const uint8_t* wexp1 =
+        GATEUP ? (F8 ? p.q1 : reinterpret_cast<const uint8_t*>(p.w1)) + (size_t)e * ncols * K * WB : wexp0;
 
     const uint16_t* asrc[AI];
-    const uint16_t* bsrc[4];
+    const uint8_t* bsrc[BI];
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int r = (BM / 8) * wave + 8 * i + lrow;
@@ -598,23 +615,23 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
       asrc[i] = p.a + (size_t)grow * K + ch * 8;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 32 * wave + 8 * i + lrow;
-      const int ch = lslot ^ tsw(r);
+    for (int i = 0; i < BI; ++i) {
+      const int r = F8 ? 32 * wave + 16 * i + qrow : 32 * wave + 8 * i + lrow;
+      const int ch = F8 ? qslot ^ ((r >> 2) & 3) : lslot ^ tsw(r);
       int wc = col0 + ((GATEUP && r >= HC) ? r - HC : r);
       if (wc >= ncols) wc = col0;                // partial column tile: any valid row
-      bsrc[i] = ((GATEUP && r >= HC) ? wexp1 : wexp0) + (size_t)wc * K + ch * 8;
+      bsrc[i] = ((GATEUP && r >= HC) ? wexp1 : wexp0) + (size_t)wc * K * WB + ch * 16;
     }
     const int ldsA = ((BM / 8) * wave) * kTBK;
-    const int ldsB = STA + (32 * wave) * kTBK;
+    const int ldsB = STA + (32 * wave) * (WRB / 2);
 
 #define MOE_DMA(BUF, KT_)                                                                          \
   {                                                                                                \
-    const int ko_ = ((KT_) < KT ? (KT_) : KT - 1) * kTBK;                                         \
+    const int kt_ = (KT_) < KT ? (KT_) : KT - 1;                                                  \
     _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                 \
-        dma16(asrc[i] + ko_, (BUF) + ldsA + 8 * i * kTBK);                                         \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
-        dma16(bsrc[i] + ko_, (BUF) + ldsB + 8 * i * kTBK);                                         \
+        dma16(asrc[i] + kt_ * kTBK, (BUF) + ldsA + 8 * i * kTBK);                                  \
+    _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                 \
+        dma16(bsrc[i] + kt_ * WRB, (BUF) + ldsB + (F8 ? 16 : 8) * i * (WRB / 2));                 \
   }
 
     f32x16_t acc[FMW][2];
@@ -641,8 +658,14 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
       u32x4_t af[FMW], bf[2];                                                                      \
       _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
           af[i] = *reinterpret_cast<const u32x4_t*>((BUF) + aoff0[s] + 32 * i * kTBK);            \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                              \
+        if constexpr (F8) {                                                                        \
+          const uint2 raw_ = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(BUF) + boff0[s] + brow0[j] * WRB); \
+          bf[j] = e4m3x8_to_bf16x8(raw_.x, raw_.y);                                                \
+        } else {                                                                                   \
           bf[j] = *reinterpret_cast<const u32x4_t*>((BUF) + boff0[s] + brow0[j] * kTBK);          \
+        }                                                                                          \
+      }                                                                                            \
       _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
           _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]); \
     }                                                                                              \
@@ -673,6 +696,15 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
       __syncthreads();
     }
 
+    // FP8: per-channel scales of this lane's columns (gate, up | the two down columns)
+    float wsc[2] = {1.f, 1.f};
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = GATEUP ? col0 + wn * 32 + fr : col0 + wn * 64 + 32 * j + fr;
+        if (col < ncols) wsc[j] = (GATEUP && j == 1 ? p.s1 : p.s0)[(size_t)e * ncols + col];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < FMW; ++i) {
 #pragma unroll
@@ -684,14 +716,14 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
           uint16_t* orow = p.out + (size_t)(GATEUP ? row0 + row : s_orow[row]) * ncols;
           if (GATEUP) {
             const int col = col0 + wn * 32 + fr;
-            const float g = acc[i][0][4 * b + q], u = acc[i][1][4 * b + q];
+            const float g = acc[i][0][4 * b + q] * wsc[0], u = acc[i][1][4 * b + q] * wsc[1];
             if (col < ncols) orow[col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
           } else {
             const float sc = s_scale[row];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const int col = col0 + wn * 64 + 32 * j + fr;
-              if (col < ncols) orow[col] = f32_to_bf16(acc[i][j][4 * b + q] * sc);
+              if (col < ncols) orow[col] = f32_to_bf16(acc[i][j][4 * b + q] * wsc[j] * sc);
             }
           }
         }
@@ -733,7 +765,7 @@ hipError_t launch_stream(const FfnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool GATEUP, int BM>
+template <bool GATEUP, int BM, bool F8>
 hipError_t launch_tile_bm(const FfnArgs& a, int num_cu, hipStream_t st) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;
   const int NT = ceil_div(a.ncols, HC);
@@ -742,19 +774,19 @@ hipError_t launch_tile_bm(const FfnArgs& a, int num_cu, hipStream_t st) {
   long grid = (num_cu / 8) * 8;
   if (ub < grid) grid = ((ub + 7) / 8) * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8>), dim3((unsigned)grid), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
 // Tile height from the mean rows per group: the smallest of 128 / 192 / 256
 // that holds 1.25x the mean, so that typical groups fill one row tile (a
 // 256-row tile over 154-row groups wastes 40% of its MFMA work).
-template <bool GATEUP>
+template <bool GATEUP, bool F8>
 hipError_t launch_tile(const FfnArgs& a, int num_cu, hipStream_t st) {
   const double need = 1.25 * (double)a.rows_total / (a.E > 0 ? a.E : 1);
-  if (need <= 128.0) return launch_tile_bm<GATEUP, 128>(a, num_cu, st);
-  if (need <= 192.0) return launch_tile_bm<GATEUP, 192>(a, num_cu, st);
-  return launch_tile_bm<GATEUP, 256>(a, num_cu, st);
+  if (need <= 128.0) return launch_tile_bm<GATEUP, 128, F8>(a, num_cu, st);
+  if (need <= 192.0) return launch_tile_bm<GATEUP, 192, F8>(a, num_cu, st);
+  return launch_tile_bm<GATEUP, 256, F8>(a, num_cu, st);
 }
 
 // The split-contraction decode kernel pays off only when the plain streaming
@@ -777,15 +809,13 @@ hipError_t launch_stream_ks(const FfnArgs& a, hipStream_t st) {
 }
 
 // Mean rows per group decides the kernel; the streaming kernel's pass height
-// covers ~1.2x the mean so that typical groups take one pass.  bf16 weights
-// switch to the tile kernel above 56 mean rows; FP8 weights stay on the
-// streaming kernel at every size (64-row passes), the only kernel that reads
-// them.
+// covers ~1.2x the mean so that typical groups take one pass; above 56 mean
+// rows the tile kernel takes over (bf16 and FP8 weights alike).
 int stream_fm(const FfnArgs& a, bool gateup) {
   const bool f8 = a.q0 != nullptr;
   if (a.K % (f8 ? 2 * kSK : kSK) != 0 || a.ncols % (4 * kSCols * (gateup ? 1 : 2)) != 0) return 0;
   const double mean = (double)a.rows_total / (a.E > 0 ? a.E : 1);
-  if (mean > 56.0 && !f8) return 0;
+  if (mean > 56.0) return 0;
   const double need = mean * 1.2;
   if (need <= 16.0) return 1;
   if (need <= 32.0) return 2;
@@ -803,11 +833,7 @@ hipError_t launch_ffn(const FfnArgs& a, int num_cu, hipStream_t st) {
     case 4: return launch_stream<4, GATEUP, F8>(a, st);
     default: break;
   }
-  if constexpr (F8) {
-    return hipErrorInvalidValue;                  // the host checks K and ncols for FP8 first
-  } else {
-    return launch_tile<GATEUP>(a, num_cu, st);
-  }
+  return launch_tile<GATEUP, F8>(a, num_cu, st);
 }
 
 }  // namespace

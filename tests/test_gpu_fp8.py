@@ -83,9 +83,11 @@ FFN_SHAPES = [
     (64, 256, 64, 8, 1024),   # 1-row groups: plain 16-row gate+up, split down
     (60, 768, 4, 2, 512),     # 48-row passes, down with 48 columns per wave
     (100, 768, 4, 2, 512),    # 64-row passes
-    (300, 256, 3, 1, 256),    # 100-row groups: two passes each
+    (300, 256, 3, 1, 256),    # 100-row groups: the tile kernel, 128-row tiles
     (50, 256, 6, 6, 256),     # k = E
     (40, 512, 16, 2, 256),    # empty experts
+    (600, 512, 4, 1, 512),    # 150-row groups: the tile kernel, 192-row tiles
+    (1200, 256, 4, 1, 256),   # 300-row groups: 256-row tiles, two row tiles per group
 ]
 
 
@@ -245,3 +247,18 @@ def test_layer_fp8_workload(name, n_tokens, experts, sample):
     mxg, l2g = errors(got, host64(outb)[toks])
     note(f"  FP8 vs bf16 weights: oracle rel_l2={l2:.3e} max_rel={mx:.3e}; GPU rel_l2={l2g:.3e}")
     assert l2 < 0.08 and l2g < 0.08
+
+
+def test_expert_node_share_fp8():
+    """16 local experts fed 32768 pre-routed rows (k = 1) with FP8 weights:
+    the tile kernel at full size, checked on sampled rows."""
+    w, d, t, gw = _workload("qwen235_node")
+    dm = moe.dims(w.N, w.M, w.E, w.k, w.H)
+    note(f"layer fp8 {w.title}")
+    out = moe.moe_layer_fp8(dm, t["x"], gw, topk_ids=t["topk_ids"], topk_weights=t["topk_weights"], ids_in=True)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(14).choice(w.N, size=32, replace=False))
+    used = sorted(set(d["topk_ids"][rows, 0].tolist()))
+    ow = _oracle_experts(d, gw, used)
+    ref = O.token_outputs({"x": d["x"], **ow}, d["topk_ids"], d["topk_weights"], rows)
+    assert_close(host64(out)[rows], ref, "expert-node rows (32 sampled)")
