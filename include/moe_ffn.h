@@ -205,8 +205,9 @@ int moe_quantize_fp8(const moe_bf16* w, int64_t rows, int32_t cols, moe_fp8* q, 
  * latency, section "router 之后还有一串动作": the grouped GEMM's cost in decode
  * is reading weights).  experts: a host pointer to the weight set.  Needs
  * hidden % 256 == 0 and expert_width % 256 == 0 (else MOE_ERR_UNSUPPORTED).
- * Workspace: moe_grouped_ffn_workspace_bytes.  All batch sizes run the
- * weight-streaming kernels (at most 64 rows per pass over the weights).
+ * Workspace: moe_grouped_ffn_workspace_bytes.  Kernels are chosen by the
+ * mean rows per expert as for bf16 weights (weight streaming for small
+ * groups, MFMA tiles for large ones).
  */
 int moe_grouped_ffn_fp8(const moe_dims* dims, const moe_bf16* x_sorted, const int32_t* expert_offsets,
                         const moe_fp8_ffn* experts, const float* row_scale, moe_bf16* y_sorted,
