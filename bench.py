@@ -65,19 +65,35 @@ def gateup_work(w, active: int, fp8: bool = False):
     return F, B
 
 
-def cpu_baseline(w, d):
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, d, budget_s: float = 20.0, max_runs: int = 5):
+    """The oracle on the host cores over the same inputs: up to five runs of
+    the whole layer while they fit in about 20 s, median reported."""
     import threadpoolctl
     from oracle import moe_oracle as O
-    t0 = time.perf_counter()
-    if w.pre_routed:
-        O.expert_node(d["x"], d["topk_ids"], d["topk_weights"], d["w_gate"], d["w_up"], d["w_down"])
-    else:
-        O.moe_layer(d, w.k, w.S, w.Hs)
-    dt = time.perf_counter() - t0
+    times = []
+    while len(times) < max_runs and sum(times) < budget_s:
+        t0 = time.perf_counter()
+        if w.pre_routed:
+            O.expert_node(d["x"], d["topk_ids"], d["topk_weights"], d["w_gate"], d["w_up"], d["w_down"])
+        else:
+            O.moe_layer(d, w.k, w.S, w.Hs)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
     return {"value": w.N / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the whole {w.title} layer (N={w.N}) once through the CPU oracle "
-                      f"(float64 expert math, float32 routing), {dt:.1f} s"}
+            "cpu_model": _cpu_model(), "runs": len(times),
+            "sample": f"the whole {w.title} layer (N={w.N}) through the CPU oracle (float64 expert math, "
+                      f"float32 routing), median of {len(times)} runs: {dt:.2f} s"}
 
 
 def cost_model(args) -> int:
@@ -85,7 +101,7 @@ def cost_model(args) -> int:
     time is linear in its batch, t_e(m) = alpha_e + beta_e * m).  For each
     workload's (M, H, E) it times moe_grouped_ffn (gate+up and down GEMMs)
     with every one of the E experts given m rows, m = 1, 2, 4, ..., 4096,
-    caches flushed before every call, and fits alpha and beta to the
+    caches flushed before every call (a 1 GiB read), and fits alpha and beta to the
     per-expert time (launch time / E) by least squares.  Also reports where a
     two-line fit (flat weight-streaming part, rising compute part) bends.
     Weights and rows are seeded normal values drawn on the device (their
@@ -95,7 +111,7 @@ def cost_model(args) -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # read (not written) before each call
     shapes = [("mixtral", 6144, 16384, 8), ("dsv2", 5120, 1536, 160), ("qwen30", 2048, 768, 128),
               ("qwen235", 4096, 1536, 128)]
     rows = [1 << i for i in range(13)]
@@ -121,7 +137,7 @@ def cost_model(args) -> int:
             ws = moe.workspace(moe.moe_grouped_ffn_workspace_bytes(d), dev)
             times = []
             for r in range(reps):
-                flush.fill_(r & 0xff)
+                flush.sum()
                 ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 ev0.record()
                 moe.moe_grouped_ffn(d, xs, off, wg, wu, wd, y_sorted=y, ws=ws)
@@ -164,8 +180,8 @@ def main() -> int:
                     help="size of the plain device copy timed after the layer (0 = skip); its GB/s is "
                          "the practical bandwidth ceiling and its counters scale FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--flush", action="store_true",
-                    help="overwrite a 1 GiB buffer before every step (outside the per-step events) "
-                         "so weights are read from HBM, and report the event-timed layer")
+                    help="read a 1 GiB buffer before every call (outside its events) so weights come "
+                         "from HBM, and report the median per-call time")
     ap.add_argument("--fp8", action="store_true",
                     help="run moe_layer_fp8: expert weights quantised once (moe_quantize_fp8, OCP E4M3 "
                          "with per-channel scales) before timing; activations and h stay bf16; no CPU "
@@ -213,7 +229,13 @@ def main() -> int:
     else:
         ids = torch.empty((w.N, w.k), dtype=torch.int32, device=dev)
         wts = torch.empty((w.N, w.k), dtype=torch.float32, device=dev)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+    # cache flush: a reduction over 1 GiB that the layer never touches; it reads
+    # (an overwrite would leave L2 and the Infinity Cache full of dirty lines
+    # whose write-back the timed call would then pay)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+
+    def flush():
+        flush_buf.sum()
     if args.fp8:
         W8 = moe.quantize_ffn_fp8(T["w_gate"], T["w_up"], T["w_down"])
         S8 = moe.quantize_ffn_fp8(T["ws_gate"], T["ws_up"], T["ws_down"]) if w.S > 0 else None
@@ -248,16 +270,18 @@ def main() -> int:
 
     for _ in range(args.warmup):
         if flush_buf is not None:
-            flush_buf.fill_(1)
+            flush()
         step()
     torch.cuda.synchronize()
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
-    for row in evs:              # torch creates the HIP event on first record
+    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for row in evs + call_ev:    # torch creates the HIP event on first record
         for e in row:
             e.record()
     torch.cuda.synchronize()
-    # timed steps: back-to-back layer calls with nothing else on the stream
+    # pass 1, timed steps: back-to-back layer calls with nothing else on the
+    # stream (skipped with --flush, whose value is the per-call median)
     wall = 0.0
     if flush_buf is None:
         t0 = time.perf_counter()
@@ -265,12 +289,23 @@ def main() -> int:
             step()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    # instrumented steps (stage events inside the layer): per-stage times and,
-    # with --flush, the layer time between its first and last event; the
-    # micro-batched layer records its whole call between two events instead
+    # pass 2, per call: each call between two events on the layer's stream;
+    # with --flush a 1 GiB buffer is read before each call, outside the events,
+    # so no weight is served from L2 or the Infinity Cache
     for i in range(K):
         if flush_buf is not None:
-            flush_buf.fill_(i & 0xff)
+            flush()
+        call_ev[i][0].record()
+        step()
+        call_ev[i][1].record()
+    torch.cuda.synchronize()
+    call_ms = np.array([call_ev[i][0].elapsed_time(call_ev[i][1]) for i in range(K)])
+    # pass 3, stages: events recorded inside the layer at its stage boundaries
+    # (each costs the stream a few us); the micro-batched layer records its
+    # whole call between two events instead
+    for i in range(K):
+        if flush_buf is not None:
+            flush()
         if pipelined:
             evs[i][0].record()
             step()
@@ -281,8 +316,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(6)] for i in range(K)])
-    layer_ms = np.array([evs[i][0].elapsed_time(evs[i][6]) for i in range(K)])
-    ms_per_step = (layer_ms.mean() if args.flush else wall * 1e3 / K)
+    ms_per_step = float(np.median(call_ms)) if args.flush else wall * 1e3 / K
     value = w.N / (ms_per_step * 1e-3)
 
     hid = ids.cpu().numpy().reshape(-1)
@@ -308,8 +342,9 @@ def main() -> int:
         "config": {"workload": w.title, "N": w.N, "M": w.M, "E": w.E, "k": w.k, "H": w.H, "S": w.S, "Hs": w.Hs,
                    "expert_weights": "fp8 e4m3, per-channel fp32 scales" if args.fp8 else "bf16",
                    "micro_batches": args.micro_batches,
-                   "parallelism": "single GPU", "timing": "event-timed, caches flushed" if args.flush
-                   else "wall clock over back-to-back steps"},
+                   "parallelism": "single GPU",
+                   "timing": "median of per-call event times, L2 and Infinity Cache flushed before each call"
+                   if args.flush else "wall clock over back-to-back steps"},
         "roofline": {"bound": "mfma" if mfma_bound else "hbm",
                      "kernel": ("whole layer, micro-batched" if pipelined else
                                 "grouped SwiGLU gate+up GEMM (ffn_stream_kernel at decode-sized experts, "
@@ -320,9 +355,9 @@ def main() -> int:
         "layer": {"flops": F, "bytes": B, "tflops": F / t_layer / 1e12, "hbm_gbs": B / t_layer / 1e9,
                   "mfma_frac": F / t_layer / (BF16_PEAK_TFLOPS * 1e12), "hbm_frac": B / t_layer / (HBM_PEAK_GBS * 1e9),
                   "roofline_frac": t_roof / t_layer, "t_roof_us": t_roof * 1e6,
-                  "event_layer_us": float(layer_ms.mean() * 1e3),
-                  # per-call spread from the instrumented pass (includes the stage events)
-                  "event_layer_us_p10_p50_p90": [float(np.percentile(layer_ms, q) * 1e3) for q in (10, 50, 90)]},
+                  # per-call times, each call between two events (caches flushed with --flush)
+                  "event_layer_us": float(call_ms.mean() * 1e3),
+                  "event_layer_us_p10_p50_p90": [float(np.percentile(call_ms, q) * 1e3) for q in (10, 50, 90)]},
         "stages_us": None if pipelined else {s: float(stage_ms[:, j].mean() * 1e3) for j, s in enumerate(STAGES)},
         "routing": {"active_experts": active, "max_rows": int(counts.max()), "mean_rows": float(counts.mean()),
                     "empty_experts": int((counts == 0).sum())},

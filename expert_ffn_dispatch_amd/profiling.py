@@ -3,6 +3,8 @@
     python -m expert_ffn_dispatch_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
     python -m expert_ffn_dispatch_amd.profiling traffic <fetch counter_collection.csv>
         <write counter_collection.csv> <kernel substring> <copy bytes> <out.txt> "<command>"
+    python -m expert_ffn_dispatch_amd.profiling counters <out.md> "<command>" "<note>"
+        <kernel substrings, comma separated> <counter_collection.csv> [...]
 
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernel,
 each scaled by bytes / counter for a plain device copy of known size run in
@@ -93,6 +95,30 @@ def summarize_traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: i
     return res
 
 
+def summarize_counters(counter_csvs, kernels, out_md: str, command: str, note: str = "") -> str:
+    """Median per dispatch of every counter in the given counter_collection
+    CSVs (one per --pmc pass) for each kernel whose name contains one of
+    `kernels`; one markdown table, kernels as columns."""
+    vals = {}
+    for path in counter_csvs:
+        for r in csv.DictReader(open(path)):
+            for k in kernels:
+                if k in r["Kernel_Name"]:
+                    vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in vals.values() for c in v})
+    lines = ["# rocprofv3 counters per dispatch (median)", "", f"command: `{command}`", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["| counter | " + " | ".join(kernels) + " |", "|---|" + "---|" * len(kernels)]
+    for c in names:
+        cells = [f"{statistics.median(vals[k][c]):.4g}" if c in vals.get(k, {}) else "-" for k in kernels]
+        lines.append(f"| {c} | " + " | ".join(cells) + " |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md, "w") as fh:
+        fh.write(text)
+    return text
+
+
 def read_traffic(path: str):
     """Parse a traffic summary; None if missing or taken on other kernel sources."""
     if not os.path.exists(path):
@@ -112,5 +138,8 @@ if __name__ == "__main__":
         print(summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif sys.argv[1] == "traffic":
         print(summarize_traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7]))
+    elif sys.argv[1] == "counters":
+        # counters <out.md> "<command>" "<note>" <kernel substrings, comma separated> <csv> [<csv> ...]
+        print(summarize_counters(sys.argv[6:], sys.argv[5].split(","), sys.argv[2], sys.argv[3], sys.argv[4]))
     else:
         raise SystemExit(__doc__)
