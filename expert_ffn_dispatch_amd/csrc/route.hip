@@ -19,8 +19,8 @@
 //               the contraction is split into KS slices so that even a
 //               decode batch spreads over many waves
 //   topk      - one wave per token: sums the KS partials in slice order
-//               (deterministic), adds the bias, wave-wide arg-max k times
-//               (ties to the lower id), renormalises.
+//               (deterministic), adds the bias, ranks every score against
+//               the others (ties to the lower id), renormalises the k best.
 #include "common.h"
 #include "kernels.h"
 
@@ -131,15 +131,34 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// Order key of (score, expert): larger keys win.  The score's bits are made
+// monotone as an unsigned integer (negative zero first becomes positive zero,
+// so that equal scores stay equal) and the expert id, inverted, breaks ties
+// in favour of the lower id.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  const uint32_t m = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)m << 32) | (uint32_t)~(uint32_t)e;
+}
+
+// One wave per token.  Each lane holds PER scores (experts lane + 64 i); the
+// token's order keys are also written to this wave's LDS row, and every lane
+// counts the keys above each of its own: that count is the score's rank, and
+// ranks 0..k-1 are the k slots.  No cross-lane reduction chains: the
+// broadcast LDS reads and 64-bit compares of all lanes run side by side.
+// The weights are exp(l - l_max) of the k winners over their sum (in slot
+// order).
 template <int PER>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part, const float* __restrict__ bias,
                                                           int N, int E, int EP, int KS, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
+  __shared__ __align__(16) uint64_t sk[4][64 * PER];
+  __shared__ float sx[4][16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = blockIdx.x * 4 + w;
+  if (n >= N) return;                    // whole waves; no block barrier below
   float v[PER];
-  bool taken[PER];
+  uint64_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
@@ -150,38 +169,49 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       if (bias) s += bias[e];
     }
     v[i] = s;
-    taken[i] = !(e < E);
+    key[i] = topk_key(s, e);
+    sk[w][e] = e < E ? key[i] : 0;       // padding loses to every expert
   }
-  int my_e = 0;
-  float my_v = 0.f;
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.f;
-    int be = 0x7fffffff;
+  // LDS operations of a wave complete in order; the barrier only keeps the
+  // compiler from moving the reads above the writes
+  __builtin_amdgcn_wave_barrier();
+  int rank[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane + 64 * i;
-      if (!taken[i] && (be == 0x7fffffff || v[i] > bv)) { bv = v[i]; be = e; }
-    }
+  for (int i = 0; i < PER; ++i) rank[i] = 0;
+  // E rounded up to pairs: a padding key (0) never counts
+  for (int j = 0; j < E; j += 4) {
+    const uint4 a = *reinterpret_cast<const uint4*>(&sk[w][j]);
+    const uint4 b = *reinterpret_cast<const uint4*>(&sk[w][j + 2]);
+    const uint64_t q[4] = {((uint64_t)a.y << 32) | a.x, ((uint64_t)a.w << 32) | a.z,
+                           ((uint64_t)b.y << 32) | b.x, ((uint64_t)b.w << 32) | b.z};
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      const bool better = (oe != 0x7fffffff) && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (better) { bv = ov; be = oe; }
-    }
-    if (lane == j) { my_e = be; my_v = bv; }
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i == be) taken[i] = true;
+      for (int i = 0; i < PER; ++i) rank[i] += q[u] > key[i] ? 1 : 0;
   }
-  const float vmax = __shfl(my_v, 0);
-  const float ex = (lane < k) ? __expf(my_v - vmax) : 0.f;
-  float s = ex;
+  // slot r of the winners: the largest score first
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (lane < k) {
-    ids[(size_t)n * k + lane] = my_e;
-    wts[(size_t)n * k + lane] = ex / s;
+  for (int i = 0; i < PER; ++i)
+    if (lane + 64 * i < E && rank[i] < k) sx[w][rank[i]] = v[i];
+  __builtin_amdgcn_wave_barrier();
+  const float vmax = sx[w][0];
+  float ex[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) ex[i] = __expf(v[i] - vmax);
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lane + 64 * i < E && rank[i] < k) sx[w][rank[i]] = ex[i];
+  __builtin_amdgcn_wave_barrier();
+  float sum = 0.f;
+  for (int r = 0; r < k; ++r) sum += sx[w][r];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E && rank[i] < k) {
+      ids[(size_t)n * k + rank[i]] = e;
+      wts[(size_t)n * k + rank[i]] = ex[i] / sum;
+    }
   }
 }
 
