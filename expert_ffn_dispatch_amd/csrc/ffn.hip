@@ -12,21 +12,23 @@
 // Phase 2 (down): y = (h W_d^T) * row_scale.
 //
 // Two kernels, chosen on the host from the mean rows per expert (N*k/E):
-//  * stream (decode-sized groups, <= 56 mean rows): every wave owns 16 output
-//    columns and streams its weight rows from HBM (row-contiguous loads two
-//    chunks ahead, staged through a wave-private LDS slot); the group's token
-//    rows (at most 64 per pass) are staged in LDS and shared by the four
-//    waves.  Weights are read once per pass; the kernel is bound by HBM
-//    bandwidth.  Blocks start their walk over the contraction at different
-//    chunks so that concurrent loads spread over DRAM channels.
-//  * tile (large groups): 256-row x 256-column tiles, both operands loaded
-//    straight into LDS in 64-wide stages (16-byte chunks XOR-swizzled by row
-//    so MFMA fragment reads are free of bank conflicts), eight waves of
-//    128 x 64.  Tiles are ordered row-tile-fastest and dealt to the eight
-//    XCDs in contiguous runs so that tiles sharing weights or rows share an
-//    L2.
+//  * stream (decode-sized groups, <= 56 mean rows): every wave owns 16 (or
+//    48) output columns and streams its weight rows from HBM (row-contiguous
+//    loads two chunks ahead, staged through a wave-private LDS slot); the
+//    group's token rows (at most 64 per pass) are staged in LDS and shared
+//    by the block's waves.  Weights are read once per pass; the kernel is
+//    bound by HBM bandwidth.  Blocks start their walk over the contraction at
+//    different chunks so that concurrent loads spread over DRAM channels.
+//  * tile (large groups): 128/192/256-row x 256-column tiles, both operands
+//    loaded straight into LDS in 64-wide stages (16-byte chunks XOR-swizzled
+//    by row so MFMA fragment reads are free of bank conflicts), eight waves
+//    of (rows/2) x 64.  Tiles are ordered row-tile-fastest and dealt to the
+//    eight XCDs in contiguous runs so that tiles sharing weights or rows share
+//    an L2.
 // Both walk a tile list built in LDS from the device-side group offsets, so
-// the host never reads the counts.
+// the host never reads the counts.  Both also take FP8 (OCP E4M3) weights
+// with one scale per output channel: the codes are widened to bf16 exactly
+// as MFMA fragments are read from LDS, and the scale multiplies the fp32 sum.
 #include <type_traits>
 
 #include "ffn_common.h"
