@@ -20,7 +20,7 @@ EXPORTS = (
     "moe_permute_workspace_bytes",
     "moe_grouped_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
     "moe_layer", "moe_set_stage_events", "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_layer_fp8",
-    "moe_layer_pipelined_workspace_bytes", "moe_layer_pipelined",
+    "moe_layer_pipelined_workspace_bytes", "moe_layer_pipelined", "moe_layer_single_launch",
 )
 MOE_STAGE_EVENTS = 7
 
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
     lib.moe_layer_pipelined_workspace_bytes.argtypes = [DIMS, ctypes.c_uint32, ctypes.c_int32,
                                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_layer_pipelined.argtypes = [DIMS, ctypes.c_uint32, ctypes.c_int32] + [P] * 13 + [ctypes.c_size_t, P]
+    lib.moe_layer_single_launch.argtypes = [DIMS, ctypes.c_uint32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib

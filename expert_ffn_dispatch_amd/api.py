@@ -45,6 +45,13 @@ def moe_layer_workspace_bytes(d: MoeDims, flags: int = 0) -> int:
     return n.value
 
 
+def moe_layer_single_launch(d: MoeDims, flags: int = 0, fp8: bool = False) -> bool:
+    """Whether moe_layer (or moe_layer_fp8) runs these dims as one launch."""
+    v = ctypes.c_int(0)
+    _lib.check(_lib.load().moe_layer_single_launch(ctypes.byref(d), flags, int(fp8), ctypes.byref(v)))
+    return bool(v.value)
+
+
 def moe_route_workspace_bytes(d: MoeDims) -> int:
     n = ctypes.c_size_t(0)
     _lib.check(_lib.load().moe_route_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))

@@ -121,7 +121,21 @@ struct LayerWs {
   uint16_t* y;
   uint16_t* hs;
   uint16_t* ys;
+  void* decode;          // single-launch decode path (router partials, barrier words)
+  bool has_decode;
 };
+// The single-launch decode path (decode.hip) is switched off: its first run
+// ended the calling process with a segmentation fault inside the layer call,
+// before any of its kernels had completed, and the fault has not been traced
+// to a cause.  Until it is, decode-sized batches run as separate kernels.
+constexpr bool kSingleLaunchDecode = false;
+
+// Shapes the single-launch decode path can take (bf16 weights; FP8 weights
+// need a subset of them).
+bool decode_shape(const moe_dims& d) {
+  return kSingleLaunchDecode && d.n_shared == 0 &&
+         moe::decode_fusable(d.n_tokens, d.hidden, d.n_experts, d.top_k, d.expert_width, false);
+}
 LayerWs carve_layer(Carver& c, const moe_dims& d) {
   const size_t N = d.n_tokens, A = (size_t)d.n_tokens * d.top_k, E = d.n_experts;
   const size_t SH = (size_t)d.n_shared * (d.n_shared > 0 ? d.shared_width : 0);
@@ -140,7 +154,23 @@ LayerWs carve_layer(Carver& c, const moe_dims& d) {
   w.y = c.take<uint16_t>(A * d.hidden);
   w.hs = SH ? c.take<uint16_t>(N * SH) : nullptr;
   w.ys = SH ? c.take<uint16_t>(N * d.hidden) : nullptr;
+  w.has_decode = decode_shape(d);
+  w.decode = w.has_decode ? c.take<char>(moe::decode_workspace_bytes(d.n_tokens, d.hidden, d.n_experts)) : nullptr;
   return w;
+}
+
+// Ticks of the device's constant-rate clock in half a second: the longest
+// wait of a grid barrier in the single-launch decode path.
+uint64_t barrier_limit_ticks() {
+  static uint64_t cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) return 0;
+    cache[dev] = (uint64_t)khz * 500;
+  }
+  return cache[dev];
 }
 
 int num_cus() {
@@ -307,6 +337,13 @@ struct GemmOrder {
 
 // Enqueue the whole layer on `st`; every argument has been checked and `ws`
 // holds carve_layer(dims).  `rec`: record the stage events.
+// True while `st` records into a graph (or its state cannot be read).
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return true;
+  return cs != hipStreamCaptureStatusNone;
+}
+
 int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_bf16* x, const moe_bf16* w_router,
                   const float* router_bias, const ExpertWeights& routed, const ExpertWeights& shared,
                   int32_t* topk_ids, float* topk_weights, moe_bf16* out, void* ws, hipStream_t st, int ncu,
@@ -318,6 +355,42 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
   int32_t* ids = topk_ids ? topk_ids : w.ids;
   float* wts = topk_weights ? topk_weights : w.wts;
   auto mark = [&](int i) -> hipError_t { return rec ? hipEventRecord(g_stage_ev[i], st) : hipSuccess; };
+
+  // Decode-sized batches: the whole layer in one launch (not while per-stage
+  // events are wanted, not between the micro-batch streams, and not under
+  // stream capture, where the kernels below are recorded instead).
+  const bool f8 = routed.qgate != nullptr;
+  if (!ids_in && !rec && w.has_decode && order.before == nullptr && order.after == nullptr &&
+      moe::decode_fusable(N, M, E, k, H, f8) && !capturing(st)) {
+    const uint64_t limit = barrier_limit_ticks();
+    if (limit == 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device clock", fn);
+    moe::DecodeArgs da{};
+    da.x = x;
+    da.w_router = w_router;
+    da.bias = router_bias;
+    da.N = N;
+    da.M = M;
+    da.E = E;
+    da.k = k;
+    da.H = H;
+    da.w_gate = routed.gate;
+    da.w_up = routed.up;
+    da.w_down = routed.down;
+    da.q_gate = routed.qgate;
+    da.q_up = routed.qup;
+    da.q_down = routed.qdown;
+    da.s_gate = routed.sgate;
+    da.s_up = routed.sup;
+    da.s_down = routed.sdown;
+    da.ids = ids;
+    da.wts = wts;
+    da.out = out;
+    da.h = w.h;
+    da.y = w.y;
+    da.limit = limit;
+    if (hipError_t e = moe::launch_decode_layer(da, w.decode, ncu, st)) return device_error(fn, e);
+    return ok();
+  }
   if (hipError_t e = mark(0)) return device_error(fn, e);
 
   if (!ids_in) {
@@ -538,6 +611,19 @@ int moe_layer_workspace_bytes(const moe_dims* dims, uint32_t flags, size_t* byte
   Carver c(nullptr);
   carve_layer(c, *dims);
   *bytes = c.off;
+  return ok();
+}
+
+int moe_layer_single_launch(const moe_dims* dims, uint32_t flags, int fp8, int* single) {
+  const char* fn = "moe_layer_single_launch";
+  if (int r = check_dims(fn, dims, true)) return r;
+  if (flags & ~uint32_t(MOE_FLAG_IDS_IN)) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+  if (single == nullptr) return fail(MOE_ERR_INVALID, "%s: single is NULL", fn);
+  *single = ((flags & MOE_FLAG_IDS_IN) == 0 && decode_shape(*dims) &&
+             moe::decode_fusable(dims->n_tokens, dims->hidden, dims->n_experts, dims->top_k, dims->expert_width,
+                                 fp8 != 0))
+                ? 1
+                : 0;
   return ok();
 }
 

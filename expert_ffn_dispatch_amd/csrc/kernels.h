@@ -77,6 +77,45 @@ hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st);
 hipError_t launch_quantize_fp8(const uint16_t* w, long long rows, int cols, uint8_t* q, float* scale,
                                hipStream_t st);
 
+// Single-launch layer for decode-sized batches (decode.hip): router, top-k,
+// permutation, grouped SwiGLU and combine in one cooperative launch with
+// grid-wide barriers.  Weights are bf16 (w_*) or FP8 codes with scales
+// (q_*, s_*).  ws holds decode_workspace_bytes(N, M, E) bytes; h and y are
+// [N*k][H] and [N*k][M].
+constexpr int kDecodeTokens = 8;
+constexpr int kDecodeAssign = 64;
+constexpr int kDecodeMaxBlocks = 1024;
+constexpr int kDecodeMaxExperts = 256;
+struct DecodeSync;
+struct DecodeArgs {
+  const uint16_t* x;         // [N][M]
+  const uint16_t* w_router;  // [M][E]
+  const float* bias;         // [E] or null
+  int N, M, E, k, H;
+  const uint16_t* w_gate;
+  const uint16_t* w_up;
+  const uint16_t* w_down;
+  const uint8_t* q_gate;
+  const uint8_t* q_up;
+  const uint8_t* q_down;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  int32_t* ids;              // [N][k] out
+  float* wts;                // [N][k] out
+  uint16_t* out;             // [N][M] out
+  uint16_t* h;
+  uint16_t* y;
+  uint64_t limit;            // longest barrier wait, in wall-clock ticks
+  // set by the launcher
+  float* part;
+  DecodeSync* sync;
+  int G, MS;
+};
+bool decode_fusable(int N, int M, int E, int k, int H, bool f8);
+size_t decode_workspace_bytes(int N, int M, int E);
+hipError_t launch_decode_layer(DecodeArgs a, void* ws, int num_cu, hipStream_t st);
+
 struct CombineArgs {
   const uint16_t* y;         // [A][M] bf16
   const int32_t* a2s;        // [A]

@@ -113,6 +113,26 @@ const char* moe_last_error(void);
 /* Workspace moe_layer needs for `dims` and `flags`, in bytes (host). */
 int moe_layer_workspace_bytes(const moe_dims* dims, uint32_t flags, size_t* bytes);
 
+/*
+ * moe_layer_single_launch - whether moe_layer (fp8 = 0) or moe_layer_fp8
+ * (fp8 != 0) runs the whole layer as one launch for these dims and flags
+ * (host only; *single = 1 or 0).  Page on MoE latency ("MoE 少算 FLOPs，延迟
+ * 反而涨了"): at decode the steps around the expert GEMMs cost latency, not
+ * FLOPs, and each kernel launch and wait adds to it.
+ *
+ * The single launch needs at most 8 tokens and 64 assignments (N*k), E in
+ * {8, 16, 32, 64, 128, 256}, M and H multiples of 128 (256 with FP8 weights),
+ * no shared experts and the router (no MOE_FLAG_IDS_IN).  It routes with fp32
+ * FMAs whose summation order differs from moe_route's, so routing weights may
+ * differ in the last bits and ids only where scores tie within rounding.
+ * It is not taken while the stream is being captured into a graph or while
+ * stage events are set; the layer then runs as separate kernels.
+ *
+ * In this build the single launch is switched off (its first run ended the
+ * calling process with a fault not yet traced): *single is always 0.
+ */
+int moe_layer_single_launch(const moe_dims* dims, uint32_t flags, int fp8, int* single);
+
 /* Workspace moe_route / moe_permute / moe_grouped_ffn need, in bytes (host).
  * For moe_grouped_ffn the dims are those of the call (E groups, N*k rows). */
 int moe_route_workspace_bytes(const moe_dims* dims, size_t* bytes);
@@ -245,6 +265,11 @@ int moe_combine(const moe_dims* dims, const moe_bf16* y_sorted, const int32_t* a
  * ws_down [M][S*Hs] (NULL iff S = 0); topk_ids [N][k] int32 and topk_weights
  * [N][k] fp32: outputs (may be NULL) or, with IDS_IN, inputs (required);
  * out [N][M] bf16.  ws: moe_layer_workspace_bytes.
+ *
+ * Decode-sized batches (moe_layer_single_launch) run as one cooperative
+ * launch instead of one kernel per step.  The workspace then also keeps a few
+ * barrier words from call to call: like every other use of a workspace,
+ * calls that share one must not overlap.
  */
 int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x,
               const moe_bf16* w_router, const float* router_bias,
