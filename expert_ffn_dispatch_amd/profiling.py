@@ -22,7 +22,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 
 # sources of the grouped expert kernels, whose launch the traffic figures describe
-FFN_SOURCES = ("ffn.hip", "ffn_common.h", "common.h", "kernels.h")
+FFN_SOURCES = ("ffn.hip", "ffn_stream.h", "ffn_common.h", "common.h", "kernels.h")
 
 
 def source_hash() -> str:
