@@ -217,3 +217,33 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_single_launch_query(lib):
+    """moe_layer_single_launch checks its arguments like the others and, with
+    the single-launch path switched off in this build, reports 0 for every
+    shape, decode-sized ones included."""
+    v = ctypes.c_int(7)
+    for n in (1, 8, 64):
+        d = _lib.MoeDims(n, 2048, 128, 8, 768, 0, 0)
+        assert lib.moe_layer_single_launch(ctypes.byref(d), 0, 0, ctypes.byref(v)) == _lib.MOE_OK
+        assert v.value == 0
+        assert lib.moe_layer_single_launch(ctypes.byref(d), 0, 1, ctypes.byref(v)) == _lib.MOE_OK
+        assert v.value == 0
+    d = _lib.MoeDims(1, 2048, 128, 8, 768, 0, 0)
+    assert lib.moe_layer_single_launch(ctypes.byref(d), 0, 0, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_layer_single_launch(ctypes.byref(d), 6, 0, ctypes.byref(v)) == _lib.MOE_ERR_INVALID
+    assert "flags" in _err(lib)
+    bad = _lib.MoeDims(1, 100, 128, 8, 768, 0, 0)
+    assert lib.moe_layer_single_launch(ctypes.byref(bad), 0, 0, ctypes.byref(v)) == _lib.MOE_ERR_INVALID
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py runs one GPU; --gpus 2 exits with a message before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "--gpus 2 is not supported" in r.stderr
+    assert r.stdout == ""
