@@ -46,6 +46,40 @@ def test_route(shape):
     assert np.abs(gw.astype(np.float64).sum(1) - 1).max() < 1e-5
 
 
+# one- and two-token batches over 64 / 128 / 256 experts: scores from W_r rows
+# with fp32 FMAs (no transpose); the larger batches check the MFMA path's
+# boundary next to it; N, M, E, k, bias
+ROW_ROUTE = [
+    (1, 2048, 128, 8, False),     # the Qwen3-30B-shaped router, one token
+    (2, 512, 64, 6, True),        # two tokens per block, bias
+    (1, 1024, 256, 8, False),     # the most experts
+    (2, 4096, 128, 8, True),      # eight slices of 512 rows
+    (1, 768, 64, 2, False),       # three slices of 256 rows
+    (1, 16384, 128, 4, False),    # slices capped at 1024 rows: 16 of them
+    (3, 2048, 128, 8, False),     # three tokens: the MFMA path
+    (32, 1024, 256, 8, True),     # the MFMA path at the most experts
+]
+
+
+@pytest.mark.parametrize("shape", ROW_ROUTE, ids=[str(s) for s in ROW_ROUTE])
+def test_route_rows(shape):
+    N, M, E, k, bias = shape
+    note(f"route rows {shape}")
+    d = gen.random_small(N, M, E, k, 128, seed=12, bias=bias, std=0.05)
+    dm = moe.dims(N, M, E, k, 128)
+    t = upload(d)
+    ids, w = moe.moe_route(dm, t["x"], t["w_router"], t.get("router_bias"))
+    ids2, w2 = moe.moe_route(dm, t["x"], t["w_router"], t.get("router_bias"))
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    r = O.route(d["x"], d["w_router"], k, d.get("router_bias"))
+    ok = r["margin"] >= TIE_MARGIN
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    assert ok.any()
+    assert np.array_equal(gi[ok], r["topk_ids"][ok])
+    np.testing.assert_allclose(gw[ok], r["topk_weights"][ok], rtol=1e-5, atol=1e-6)
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s[:5]) for s in SHAPES])
 def test_permute_bit_exact(shape):
     d, dm = _case(shape)
