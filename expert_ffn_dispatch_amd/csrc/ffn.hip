@@ -210,17 +210,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_stream_kernel(FfnArgs p) 
       if (AFULL || tid + NTH * i < RB * ACH) ra[i] = *reinterpret_cast<const ARow*>(p.a + aoff[i] + ka);
     const uint16_t* L = sa[NABUF == 1 ? 0 : (c & 1)];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int ch = s * 4 + (lane >> 4);
-      u32x4_t bf[NMAT];
+    for (int s = 0; s < (F8 ? NSUB / 2 : NSUB); ++s) {
+      // FP8: s counts pairs of sub-steps (weight_pair_f8)
+      u32x4_t bf[NMAT][F8 ? 2 : 1];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) bf[m] = weight_fragment<F8>(&sb[wave][m][0], s, lane);
+      for (int m = 0; m < NMAT; ++m) {
+        if constexpr (F8) weight_pair_f8(&sb[wave][m][0], s, lane, bf[m][0], bf[m][F8 ? 1 : 0]);
+        else bf[m][0] = weight_fragment<F8>(&sb[wave][m][0], s, lane);
+      }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = i * 16 + fr;
-        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&L[r * KC + ((ch ^ (r & 15)) << 3)]);
+      for (int h = 0; h < (F8 ? 2 : 1); ++h) {
+        const int ch = F8 ? 8 * s + 2 * (lane >> 4) + h : s * 4 + (lane >> 4);
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) acc[m][i] = mfma16(af, bf[m], acc[m][i]);
+        for (int i = 0; i < FM; ++i) {
+          const int r = i * 16 + fr;
+          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&L[r * KC + ((ch ^ (r & 15)) << 3)]);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) acc[m][i] = mfma16(af, bf[m][h], acc[m][i]);
+        }
       }
     }
     // chunk c+1 (oldest registers) into this wave's LDS slot, after this

@@ -38,6 +38,25 @@ __device__ __forceinline__ u32x4_t weight_fragment(const uint16_t* slot, int s, 
   }
 }
 
+// FP8 weights, two MFMA sub-steps at a time.  Within a chunk the order in
+// which contraction elements meet the MFMA is free as long as the token-row
+// fragments follow it, so sub-steps 2 s2 and 2 s2 + 1 give lane group g the
+// 16 contraction elements 64 s2 + 16 g .. +15: its codes are one 16-byte
+// piece of the slot row (piece 4 s2 + g, read at (4 s2 + g) ^ row), the low
+// eight for the first sub-step and the high eight for the second, and its
+// token-row pieces (8 bf16 each) are 8 s2 + 2 g and 8 s2 + 2 g + 1.  One
+// 128-bit LDS read serves two sub-steps, and a 16-lane group of it touches 16
+// different pieces of 16 rows, like the bf16 fragments (the 64-bit reads of
+// one sub-step at a time hit LDS bank conflicts: measured 65% of the
+// LDS-active cycles of the FP8 gate+up launch).
+__device__ __forceinline__ void weight_pair_f8(const uint16_t* slot, int s2, int lane, u32x4_t& lo, u32x4_t& hi) {
+  const int fr = lane & 15, q = 4 * s2 + (lane >> 4);
+  const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(slot) + fr * kRowBytes +
+                                                    ((q ^ fr) << 4));
+  lo = e4m3x8_to_bf16x8(raw.x, raw.y);
+  hi = e4m3x8_to_bf16x8(raw.z, raw.w);
+}
+
 // 16 bytes of a weight row.  NTL marks the load non-temporal: every weight
 // byte is read once per launch, and the hint keeps it from pushing the token
 // rows and h out of the caches.  Measured: gate+up streams 4-6% faster with
@@ -154,12 +173,28 @@ __device__ __forceinline__ void ks_tile(const FfnArgs& p, const int* s_off, cons
       }
     }
     for (int c = 0; c < L; ++c) {
+      if constexpr (F8) {
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        const int ch = s * 4 + (lane >> 4);
-        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&lds.sa[wave][fr * KC + ((ch ^ fr) << 3)]);
-        acc0 = mfma16(af, weight_fragment<F8>(&lds.sb[wave][0][0], s, lane), acc0);
-        acc1 = mfma16(af, weight_fragment<F8>(&lds.sb[wave][1][0], s, lane), acc1);
+        for (int s2 = 0; s2 < NSUB / 2; ++s2) {
+          u32x4_t b0[2], b1[2];
+          weight_pair_f8(&lds.sb[wave][0][0], s2, lane, b0[0], b0[1]);
+          weight_pair_f8(&lds.sb[wave][1][0], s2, lane, b1[0], b1[1]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int ch = 8 * s2 + 2 * (lane >> 4) + h;
+            const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&lds.sa[wave][fr * KC + ((ch ^ fr) << 3)]);
+            acc0 = mfma16(af, b0[h], acc0);
+            acc1 = mfma16(af, b1[h], acc1);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          const int ch = s * 4 + (lane >> 4);
+          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&lds.sa[wave][fr * KC + ((ch ^ fr) << 3)]);
+          acc0 = mfma16(af, weight_fragment<F8>(&lds.sb[wave][0][0], s, lane), acc0);
+          acc1 = mfma16(af, weight_fragment<F8>(&lds.sb[wave][1][0], s, lane), acc1);
+        }
       }
       // same wave: LDS operations complete in order, so the slot can be
       // overwritten right after this wave's reads
