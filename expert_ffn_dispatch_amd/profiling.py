@@ -4,7 +4,7 @@
     python -m expert_ffn_dispatch_amd.profiling traffic <fetch counter_collection.csv>
         <write counter_collection.csv> <kernel substring> <copy bytes> <out.txt> "<command>"
     python -m expert_ffn_dispatch_amd.profiling counters <out.md> "<command>" "<note>"
-        <kernel substrings, comma separated> <counter_collection.csv> [...]
+        <kernel substrings, separated by ;> <counter_collection.csv> [...]
 
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernel,
 each scaled by bytes / counter for a plain device copy of known size run in
@@ -139,7 +139,7 @@ if __name__ == "__main__":
     elif sys.argv[1] == "traffic":
         print(summarize_traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7]))
     elif sys.argv[1] == "counters":
-        # counters <out.md> "<command>" "<note>" <kernel substrings, comma separated> <csv> [<csv> ...]
-        print(summarize_counters(sys.argv[6:], sys.argv[5].split(","), sys.argv[2], sys.argv[3], sys.argv[4]))
+        # counters <out.md> "<command>" "<note>" <kernel substrings separated by ;> <csv> [<csv> ...]
+        print(summarize_counters(sys.argv[6:], sys.argv[5].split(";"), sys.argv[2], sys.argv[3], sys.argv[4]))
     else:
         raise SystemExit(__doc__)
