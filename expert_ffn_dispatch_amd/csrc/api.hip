@@ -406,26 +406,30 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
     if (hipError_t e = hipStreamWaitEvent(st, order.before, 0)) return device_error(fn, e);
   }
 
-  if (dims->n_shared > 0) {
+  // Shared experts: one group of all N rows, gate+up then down.  They go
+  // into the routed experts' launches (moe::launch_ffn_*_shared), so the
+  // "shared" stage between marks 2 and 3 is empty and its time counts in
+  // the gate+up and down stages.
+  const bool has_shared = dims->n_shared > 0;
+  moe::FfnArgs sg{}, sd{};
+  if (has_shared) {
     const int SH = dims->n_shared * dims->shared_width;
-    moe::FfnArgs g = gateup_args(shared);
-    g.a = x;
-    g.fixed_rows = N;
-    g.out = w.hs;
-    g.E = 1;
-    g.rows_total = N;
-    g.K = M;
-    g.ncols = SH;
-    if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
-    moe::FfnArgs dn = down_args(shared);
-    dn.a = w.hs;
-    dn.fixed_rows = N;
-    dn.out = w.ys;
-    dn.E = 1;
-    dn.rows_total = N;
-    dn.K = SH;
-    dn.ncols = M;
-    if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+    sg = gateup_args(shared);
+    sg.a = x;
+    sg.fixed_rows = N;
+    sg.out = w.hs;
+    sg.E = 1;
+    sg.rows_total = N;
+    sg.K = M;
+    sg.ncols = SH;
+    sd = down_args(shared);
+    sd.a = w.hs;
+    sd.fixed_rows = N;
+    sd.out = w.ys;
+    sd.E = 1;
+    sd.rows_total = N;
+    sd.K = SH;
+    sd.ncols = M;
   }
   if (hipError_t e = mark(3)) return device_error(fn, e);
   moe::FfnArgs g = gateup_args(routed);
@@ -437,7 +441,8 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
   g.rows_total = A;
   g.K = M;
   g.ncols = H;
-  if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
+  if (hipError_t e = has_shared ? moe::launch_ffn_gateup_shared(g, sg, ncu, st) : moe::launch_ffn_gateup(g, ncu, st))
+    return device_error(fn, e);
   if (hipError_t e = mark(4)) return device_error(fn, e);
   // top-1 routing without shared experts: every token has exactly one row,
   // so the down GEMM stores it straight into the output (the combine would
@@ -453,7 +458,8 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
   dn.K = H;
   dn.ncols = M;
   dn.out_rows = direct ? w.row_token : nullptr;
-  if (hipError_t e = moe::launch_ffn_down(dn, ncu, st)) return device_error(fn, e);
+  if (hipError_t e = has_shared ? moe::launch_ffn_down_shared(dn, sd, ncu, st) : moe::launch_ffn_down(dn, ncu, st))
+    return device_error(fn, e);
   if (order.after != nullptr) {
     if (hipError_t e = hipEventRecord(order.after, st)) return device_error(fn, e);
   }

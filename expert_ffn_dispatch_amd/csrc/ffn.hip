@@ -370,7 +370,7 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint16_t* lds) {
 // reads its eight codes of a B fragment and widens them to bf16 exactly, and
 // the per-channel scales multiply the sums in the epilogue.
 template <bool GATEUP, int BM, bool F8>
-__global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
+__global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
   constexpr int FMW = BM / 64;                   // 32-row MFMA blocks per wave
   constexpr int AI = BM / 64;                    // direct loads of token rows per wave per stage
@@ -385,10 +385,14 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;       // 2 x 4 waves
-  const int K = p.K, ncols = p.ncols;
-  const int NT = ceil_div(ncols, HC);            // the last column tile may be partial
-  const int KT = K / kTBK;
-  const int total = build_tile_list<BM>(p, NT, s_off, s_tp);
+  // p2 (if p2.E == 1): one group of p2.fixed_rows rows, the shared experts,
+  // whose tiles are dealt first; then the routed groups of p.  One launch for
+  // both spreads the shared tiles over the routed rounds instead of ending
+  // each launch on a partly empty round.
+  const int NT = ceil_div(p.ncols, HC);          // the last column tile may be partial
+  const int RT2 = p2.E > 0 ? ceil_div(p2.fixed_rows, BM) : 0;
+  const int T2 = RT2 * ceil_div(p2.ncols, HC);
+  const int total = T2 + build_tile_list<BM>(p, NT, s_off, s_tp);
   const int G = gridDim.x;                       // a multiple of 8
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int fr = lane & 31, fg = lane >> 5;
@@ -416,19 +420,32 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
   for (int round = 0; round * G < total; ++round) {
     const int tile = round * G + slot;
     if (tile >= total) continue;
-    const int e = find_group(s_tp, p.E, tile);
-    const int cnt = s_off[e + 1] - s_off[e];
-    const int RT = ceil_div(cnt, BM);
-    const int local = tile - s_tp[e];
+    const bool seg2 = tile < T2;
+    const FfnArgs& pa = seg2 ? p2 : p;
+    const int K = pa.K, ncols = pa.ncols, KT = K / kTBK;
+    int e = 0, cnt, RT, local, base;
+    if (seg2) {
+      cnt = p2.fixed_rows;
+      RT = RT2;
+      local = tile;
+      base = 0;
+    } else {
+      const int t1 = tile - T2;
+      e = find_group(s_tp, p.E, t1);
+      cnt = s_off[e + 1] - s_off[e];
+      RT = ceil_div(cnt, BM);
+      local = t1 - s_tp[e];
+      base = s_off[e];
+    }
     const int ct = local / RT, rt = local - ct * RT;
-    const int row0 = s_off[e] + rt * BM;
+    const int row0 = base + rt * BM;
     const int nrows = min(BM, cnt - rt * BM);
     const int col0 = ct * HC;
     // weight rows as bytes (bf16: 2 per element, FP8: 1)
     constexpr int WB = F8 ? 1 : 2;
-    const uint8_t* wexp0 = (F8 ? p.q0 : reinterpret_cast<const uint8_t*>(p.w0)) + (size_t)e * ncols * K * WB;
+    const uint8_t* wexp0 = (F8 ? pa.q0 : reinterpret_cast<const uint8_t*>(pa.w0)) + (size_t)e * ncols * K * WB;
     const uint8_t* wexp1 =
-        GATEUP ? (F8 ? p.q1 : reinterpret_cast<const uint8_t*>(p.w1)) + (size_t)e * ncols * K * WB : wexp0;
+        GATEUP ? (F8 ? pa.q1 : reinterpret_cast<const uint8_t*>(pa.w1)) + (size_t)e * ncols * K * WB : wexp0;
 
     const uint16_t* asrc[AI];
     const uint8_t* bsrc[BI];
@@ -437,8 +454,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
       const int r = (BM / 8) * wave + 8 * i + lrow;
       const int ch = lslot ^ tsw(r);
       const int rr = (r < nrows) ? r : 0;
-      const int grow = p.a_rows ? p.a_rows[row0 + rr] : (row0 + rr);
-      asrc[i] = p.a + (size_t)grow * K + ch * 8;
+      const int grow = pa.a_rows ? pa.a_rows[row0 + rr] : (row0 + rr);
+      asrc[i] = pa.a + (size_t)grow * K + ch * 8;
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
@@ -516,8 +533,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
     if (!GATEUP) {
       __syncthreads();
       if (tid < BM) {
-        s_scale[tid] = (p.row_scale && tid < nrows) ? p.row_scale[row0 + tid] : 1.f;
-        s_orow[tid] = (p.out_rows && tid < nrows) ? p.out_rows[row0 + tid] : row0 + tid;
+        s_scale[tid] = (pa.row_scale && tid < nrows) ? pa.row_scale[row0 + tid] : 1.f;
+        s_orow[tid] = (pa.out_rows && tid < nrows) ? pa.out_rows[row0 + tid] : row0 + tid;
       }
       __syncthreads();
     }
@@ -528,7 +545,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = GATEUP ? col0 + wn * 32 + fr : col0 + wn * 64 + 32 * j + fr;
-        if (col < ncols) wsc[j] = (GATEUP && j == 1 ? p.s1 : p.s0)[(size_t)e * ncols + col];
+        if (col < ncols) wsc[j] = (GATEUP && j == 1 ? pa.s1 : pa.s0)[(size_t)e * ncols + col];
       }
     }
 #pragma unroll
@@ -539,7 +556,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p) {
         for (int q = 0; q < 4; ++q) {
           const int row = wm * (BM / 2) + 32 * i + 8 * b + 4 * fg + q;
           if (row >= nrows) continue;
-          uint16_t* orow = p.out + (size_t)(GATEUP ? row0 + row : s_orow[row]) * ncols;
+          uint16_t* orow = pa.out + (size_t)(GATEUP ? row0 + row : s_orow[row]) * ncols;
           if (GATEUP) {
             const int col = col0 + wn * 32 + fr;
             const float g = acc[i][0][4 * b + q] * wsc[0], u = acc[i][1][4 * b + q] * wsc[1];
@@ -605,27 +622,29 @@ hipError_t launch_stream(const FfnArgs& a, hipStream_t st) {
 }
 
 template <bool GATEUP, int BM, bool F8>
-hipError_t launch_tile_bm(const FfnArgs& a, int num_cu, hipStream_t st) {
+hipError_t launch_tile_bm(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipStream_t st) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;
   const int NT = ceil_div(a.ncols, HC);
   const long ub_rows = a.rows_total / BM + (a.E < a.rows_total ? a.E : a.rows_total);
-  const long ub = ub_rows * NT;
+  const long ub = ub_rows * NT + (a2.E > 0 ? (long)ceil_div(a2.fixed_rows, BM) * ceil_div(a2.ncols, HC) : 0);
   long grid = (num_cu / 8) * 8;
   if (ub < grid) grid = ((ub + 7) / 8) * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
   return hipGetLastError();
 }
 
 // Tile height from the mean rows per group: the smallest of 128 / 192 / 256
 // that holds 1.25x the mean, so that typical groups fill one row tile (a
 // 256-row tile over 154-row groups wastes 40% of its MFMA work).
+// a2: an optional single-group segment (a2.E == 1, a2.fixed_rows rows) run
+// in the same launch, with the tile height chosen for a.
 template <bool GATEUP, bool F8>
-hipError_t launch_tile(const FfnArgs& a, int num_cu, hipStream_t st) {
+hipError_t launch_tile(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipStream_t st) {
   const double need = 1.25 * (double)a.rows_total / (a.E > 0 ? a.E : 1);
-  if (need <= 128.0) return launch_tile_bm<GATEUP, 128, F8>(a, num_cu, st);
-  if (need <= 192.0) return launch_tile_bm<GATEUP, 192, F8>(a, num_cu, st);
-  return launch_tile_bm<GATEUP, 256, F8>(a, num_cu, st);
+  if (need <= 128.0) return launch_tile_bm<GATEUP, 128, F8>(a, a2, num_cu, st);
+  if (need <= 192.0) return launch_tile_bm<GATEUP, 192, F8>(a, a2, num_cu, st);
+  return launch_tile_bm<GATEUP, 256, F8>(a, a2, num_cu, st);
 }
 
 // The split-contraction decode kernel pays off only when the plain streaming
@@ -672,7 +691,27 @@ hipError_t launch_ffn(const FfnArgs& a, int num_cu, hipStream_t st) {
     case 4: return launch_stream<4, GATEUP, F8>(a, st);
     default: break;
   }
-  return launch_tile<GATEUP, F8>(a, num_cu, st);
+  return launch_tile<GATEUP, F8>(a, FfnArgs{}, num_cu, st);
+}
+
+// Routed groups and the shared experts (one group of all rows): one tile
+// launch when both take the tile kernel with the same weight type, else the
+// shared launch and then the routed one.
+template <bool GATEUP>
+hipError_t launch_ffn_with_shared(const FfnArgs& routed, const FfnArgs& shared, int num_cu, hipStream_t st) {
+  const bool f8 = routed.q0 != nullptr;
+  if (routed.rows_total > 0 && f8 == (shared.q0 != nullptr) && stream_fm(routed, GATEUP) == 0 &&
+      stream_fm(shared, GATEUP) == 0) {
+    return f8 ? launch_tile<GATEUP, true>(routed, shared, num_cu, st)
+              : launch_tile<GATEUP, false>(routed, shared, num_cu, st);
+  }
+  if (shared.rows_total > 0) {
+    const hipError_t e = shared.q0 ? launch_ffn<GATEUP, true>(shared, num_cu, st)
+                                   : launch_ffn<GATEUP, false>(shared, num_cu, st);
+    if (e != hipSuccess) return e;
+  }
+  if (routed.rows_total == 0) return hipSuccess;
+  return f8 ? launch_ffn<GATEUP, true>(routed, num_cu, st) : launch_ffn<GATEUP, false>(routed, num_cu, st);
 }
 
 }  // namespace
@@ -685,6 +724,14 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st) {
 hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st) {
   if (a.rows_total == 0) return hipSuccess;
   return a.q0 ? launch_ffn<false, true>(a, num_cu, st) : launch_ffn<false, false>(a, num_cu, st);
+}
+
+hipError_t launch_ffn_gateup_shared(const FfnArgs& routed, const FfnArgs& shared, int num_cu, hipStream_t st) {
+  return launch_ffn_with_shared<true>(routed, shared, num_cu, st);
+}
+
+hipError_t launch_ffn_down_shared(const FfnArgs& routed, const FfnArgs& shared, int num_cu, hipStream_t st) {
+  return launch_ffn_with_shared<false>(routed, shared, num_cu, st);
 }
 
 }  // namespace moe

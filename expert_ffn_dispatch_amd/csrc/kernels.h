@@ -70,6 +70,10 @@ struct FfnArgs {
 };
 hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st);
+// The routed groups together with the shared experts (shared: E = 1,
+// fixed_rows = N): one launch where both take the tile kernel, else two.
+hipError_t launch_ffn_gateup_shared(const FfnArgs& routed, const FfnArgs& shared, int num_cu, hipStream_t st);
+hipError_t launch_ffn_down_shared(const FfnArgs& routed, const FfnArgs& shared, int num_cu, hipStream_t st);
 
 // Per-row OCP E4M3 quantisation: scale[r] = max_k |w[r][k]| / 448 (1 for a
 // zero row), q[r][k] = E4M3 nearest to w[r][k] / scale[r], ties to even,

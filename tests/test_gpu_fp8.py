@@ -115,6 +115,7 @@ LAYER_SHAPES = [
     (130, 512, 20, 1, 256, 0, 0, True),     # k = 1: the down GEMM writes the output rows
     (200, 256, 16, 2, 256, 2, 128, False),  # shared experts (concatenated width 256)
     (1, 512, 32, 4, 768, 1, 256, False),    # one token
+    (512, 256, 8, 2, 256, 2, 128, False),   # tile kernel with the shared experts in the same launch
 ]
 
 

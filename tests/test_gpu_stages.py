@@ -22,6 +22,8 @@ SHAPES = [
     (77, 256, 1, 1, 384, 0, 0, False),      # E = 1
     (200, 256, 160, 6, 128, 2, 64, False),  # many experts (some empty), shared
     (300, 512, 128, 8, 256, 1, 128, True),  # several permutation tiles, > 64 experts
+    (333, 256, 8, 2, 256, 2, 128, False),   # tile kernel with the shared experts in the same launch, ragged
+    (600, 256, 6, 3, 384, 1, 256, True),    # the same with 256-row tiles
 ]
 
 
