@@ -87,7 +87,8 @@ FFN_SHAPES = [
     (50, 256, 6, 6, 256),     # k = E
     (40, 512, 16, 2, 256),    # empty experts
     (600, 512, 4, 1, 512),    # 150-row groups: the tile kernel, 192-row tiles
-    (1200, 256, 4, 1, 256),   # 300-row groups: 256-row tiles, two row tiles per group
+    (1200, 256, 4, 1, 256),   # 300-row groups: 192-row tiles, two row tiles per group
+    (3000, 256, 4, 1, 256),   # 750-row groups: 256-row tiles, three row tiles per group
 ]
 
 

@@ -23,7 +23,8 @@ SHAPES = [
     (200, 256, 160, 6, 128, 2, 64, False),  # many experts (some empty), shared
     (300, 512, 128, 8, 256, 1, 128, True),  # several permutation tiles, > 64 experts
     (333, 256, 8, 2, 256, 2, 128, False),   # tile kernel with the shared experts in the same launch, ragged
-    (600, 256, 6, 3, 384, 1, 256, True),    # the same with 256-row tiles
+    (600, 256, 6, 3, 384, 1, 256, True),    # the same with 192-row tiles, 300-row groups
+    (1800, 256, 6, 3, 384, 1, 256, True),   # the same with 256-row tiles, 900-row groups
 ]
 
 
