@@ -435,6 +435,7 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
   moe::FfnArgs g = gateup_args(routed);
   g.a = x;
   g.a_rows = w.row_token;
+  g.a_nrows = N;
   g.offsets = w.offsets;
   g.out = w.h;
   g.E = E;

@@ -355,6 +355,15 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
 __device__ __forceinline__ void dma16(const uint8_t* g, uint16_t* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
+// The same through a buffer resource: byte `voff + soff` of the buffer
+// (per-lane and scalar parts kept apart, so that the compiler cannot turn them
+// into 64-bit per-lane pointers; reads past `bytes` return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
 
 // s_waitcnt for vector-memory count N only (expcnt and lgkmcnt left at their maxima)
 #define MOE_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | 0x0F70)
@@ -369,21 +378,32 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint16_t* lds) {
 // (four 16-byte pieces, piece c of row r at c ^ ((r >> 2) & 3)); each lane
 // reads its eight codes of a B fragment and widens them to bf16 exactly, and
 // the per-channel scales multiply the sums in the epilogue.
-template <bool GATEUP, int BM, bool F8>
+// A32: the token matrix of every segment spans less than 4 GiB, so token
+// rows are addressed by 32-bit offsets through a buffer resource; otherwise
+// by 64-bit pointers (more registers, used with 128-row tiles only).
+template <bool GATEUP, int BM, bool F8, bool A32>
 __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
   constexpr int FMW = BM / 64;                   // 32-row MFMA blocks per wave
   constexpr int AI = BM / 64;                    // direct loads of token rows per wave per stage
   constexpr int BI = F8 ? 2 : 4;                 // direct loads of weight rows per wave per stage
-  constexpr int STA = BM * kTBK;                 // bf16 elements of the token-row part
+  constexpr int STA = BM * kTBK;                 // bf16 elements of a token-row stage
   constexpr int WRB = F8 ? kTBK : 2 * kTBK;      // bytes of a weight row per stage
-  constexpr int STG = STA + kTN * WRB / 2;       // 16-bit elements per stage
-  __shared__ __align__(16) uint16_t sr0[STG];
-  __shared__ __align__(16) uint16_t sr1[STG];
+  constexpr int STB = kTN * WRB / 2;             // 16-bit elements of a weight stage
+  // Two buffers each for token and weight rows, one stage loaded ahead.
+  // Every buffer is an array of its own: the compiler then knows that loads
+  // into one buffer do not touch the reads of another (as parts of one array
+  // it waits for the loads before every read).
+  __shared__ __align__(16) uint16_t sa0[STA];
+  __shared__ __align__(16) uint16_t sa1[STA];
+  __shared__ __align__(16) uint16_t sb0[STB];
+  __shared__ __align__(16) uint16_t sb1[STB];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_tp[kMaxGroups + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: the weight rows a wave loads come from one
+  // matrix, so their base address stays in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;       // 2 x 4 waves
   // p2 (if p2.E == 1): one group of p2.fixed_rows rows, the shared experts,
   // whose tiles are dealt first; then the routed groups of p.  One launch for
@@ -403,8 +423,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     aoff0[s] = (wm * (BM / 2) + fr) * kTBK + (((2 * s + fg) ^ swf) << 3);
-    boff0[s] = F8 ? 2 * STA + fr * WRB + ((s ^ ((fr >> 2) & 3)) << 4) + (fg << 3)
-                  : STA + fr * kTBK + (((2 * s + fg) ^ swf) << 3);
+    boff0[s] = F8 ? fr * WRB + ((s ^ ((fr >> 2) & 3)) << 4) + (fg << 3)
+                  : fr * kTBK + (((2 * s + fg) ^ swf) << 3);
   }
   int brow0[2];
 #pragma unroll
@@ -447,15 +467,23 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     const uint8_t* wexp1 =
         GATEUP ? (F8 ? pa.q1 : reinterpret_cast<const uint8_t*>(pa.w1)) + (size_t)e * ncols * K * WB : wexp0;
 
-    const uint16_t* asrc[AI];
-    const uint8_t* bsrc[BI];
+    // token rows: 32-bit byte offsets into the token matrix (A32), else pointers
+    const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(pa.a, A32 ? pa.a_bytes : 0u);
+    uint32_t aoffg[AI];
+    const uint16_t* asrc[A32 ? 1 : AI];
+    // weight rows: one base per wave (rows 32 wave .. 32 wave + 31 lie all in
+    // the gate or all in the up half of the tile) and 32-bit offsets per lane
+    const __amdgpu_buffer_rsrc_t wrsrc =
+        buffer_rsrc((GATEUP && 32 * wave >= HC) ? wexp1 : wexp0, (uint32_t)ncols * (uint32_t)(K * WB));
+    uint32_t boffg[BI];
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int r = (BM / 8) * wave + 8 * i + lrow;
       const int ch = lslot ^ tsw(r);
       const int rr = (r < nrows) ? r : 0;
       const int grow = pa.a_rows ? pa.a_rows[row0 + rr] : (row0 + rr);
-      asrc[i] = pa.a + (size_t)grow * K + ch * 8;
+      if constexpr (A32) aoffg[i] = (uint32_t)grow * (uint32_t)(2 * K) + (uint32_t)(ch * 16);
+      else asrc[i] = pa.a + (size_t)grow * K + ch * 8;
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
@@ -463,19 +491,19 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       const int ch = F8 ? qslot ^ ((r >> 2) & 3) : lslot ^ tsw(r);
       int wc = col0 + ((GATEUP && r >= HC) ? r - HC : r);
       if (wc >= ncols) wc = col0;                // partial column tile: any valid row
-      bsrc[i] = ((GATEUP && r >= HC) ? wexp1 : wexp0) + (size_t)wc * K * WB + ch * 16;
+      boffg[i] = (uint32_t)wc * (uint32_t)(K * WB) + (uint32_t)(ch * 16);
     }
     const int ldsA = ((BM / 8) * wave) * kTBK;
-    const int ldsB = STA + (32 * wave) * (WRB / 2);
+    const int ldsB = (32 * wave) * (WRB / 2);
 
-#define MOE_DMA(BUF, KT_)                                                                          \
-  {                                                                                                \
-    const int kt_ = (KT_) < KT ? (KT_) : KT - 1;                                                  \
-    _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                 \
-        dma16(asrc[i] + kt_ * kTBK, (BUF) + ldsA + 8 * i * kTBK);                                  \
-    _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                 \
-        dma16(bsrc[i] + kt_ * WRB, (BUF) + ldsB + (F8 ? 16 : 8) * i * (WRB / 2));                 \
+#define MOE_DMA_A(BUF, KT_)                                                                        \
+  _Pragma("unroll") for (int i = 0; i < AI; ++i) {                                                 \
+    if constexpr (A32) dma16(arsrc, aoffg[i], (uint32_t)((KT_) * 2 * kTBK), (BUF) + ldsA + 8 * i * kTBK); \
+    else dma16(asrc[i] + (KT_) * kTBK, (BUF) + ldsA + 8 * i * kTBK);                              \
   }
+#define MOE_DMA_B(BUF, KT_)                                                                        \
+  _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                   \
+      dma16(wrsrc, boffg[i], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * i * (WRB / 2));
 
     f32x16_t acc[FMW][2];
 #pragma unroll
@@ -487,26 +515,34 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 
     // the previous tile's last reads of the buffers are done
     __syncthreads();
-    MOE_DMA(sr0, 0)
+    MOE_DMA_A(sa0, 0)
+    MOE_DMA_B(sb0, 0)
 
-    // one stage: wait for this wave's loads of stage KT_, publish it with the
-    // barrier, start stage KT_+1 into the other buffer (every wave finished
-    // reading it before the barrier), multiply stage KT_
-#define MOE_TSTEP(BUF, NBUF, KT_)                                                                  \
+    // One stage: wait for this wave's loads of stage KT_, publish them with
+    // the barrier, start stage KT_+1 into the other buffers (every wave
+    // finished reading them before the barrier; nothing past the last stage),
+    // multiply stage KT_.  The scheduling barrier keeps the loads ahead of
+    // the multiplications (left to itself the compiler sinks them to the end
+    // of the step, where they no longer overlap anything).
+#define MOE_TSTEP(ABUF, NABUF, BBUF, NBBUF, KT_)                                                   \
   {                                                                                                \
     MOE_WAIT_VM(0);                                                                                \
     __builtin_amdgcn_s_barrier();                                                                  \
-    MOE_DMA(NBUF, (KT_) + 1)                                                                       \
+    if ((KT_) + 1 < KT) {                                                                          \
+      MOE_DMA_A(NABUF, (KT_) + 1)                                                                  \
+      MOE_DMA_B(NBBUF, (KT_) + 1)                                                                  \
+    }                                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                             \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                                \
       u32x4_t af[FMW], bf[2];                                                                      \
       _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
-          af[i] = *reinterpret_cast<const u32x4_t*>((BUF) + aoff0[s] + 32 * i * kTBK);            \
+          af[i] = *reinterpret_cast<const u32x4_t*>((ABUF) + aoff0[s] + 32 * i * kTBK);           \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                              \
         if constexpr (F8) {                                                                        \
-          const uint2 raw_ = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(BUF) + boff0[s] + brow0[j] * WRB); \
+          const uint2 raw_ = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(BBUF) + boff0[s] + brow0[j] * WRB); \
           bf[j] = e4m3x8_to_bf16x8(raw_.x, raw_.y);                                                \
         } else {                                                                                   \
-          bf[j] = *reinterpret_cast<const u32x4_t*>((BUF) + boff0[s] + brow0[j] * kTBK);          \
+          bf[j] = *reinterpret_cast<const u32x4_t*>((BBUF) + boff0[s] + brow0[j] * kTBK);         \
         }                                                                                          \
       }                                                                                            \
       _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
@@ -516,20 +552,21 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   }
 
     // the loop names each buffer explicitly (see above); an odd stage count
-    // ends with one more step on the first buffer
+    // ends with one more step on the first buffers
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
-      MOE_TSTEP(sr0, sr1, kt)
-      MOE_TSTEP(sr1, sr0, kt + 1)
+      MOE_TSTEP(sa0, sa1, sb0, sb1, kt)
+      MOE_TSTEP(sa1, sa0, sb1, sb0, kt + 1)
     }
-    if (kt < KT) MOE_TSTEP(sr0, sr1, kt)
+    if (kt < KT) MOE_TSTEP(sa0, sa1, sb0, sb1, kt)
 #undef MOE_TSTEP
-#undef MOE_DMA
+#undef MOE_DMA_A
+#undef MOE_DMA_B
     MOE_WAIT_VM(0);
-    // down: the tile's row scales through LDS (the first buffer is free once
-    // every wave has finished its last stage)
-    float* s_scale = reinterpret_cast<float*>(sr0);
-    int* s_orow = reinterpret_cast<int*>(sr0) + BM;
+    // down: the tile's row scales through LDS (the first token buffer is
+    // free once every wave has finished its last stage)
+    float* s_scale = reinterpret_cast<float*>(sa0);
+    int* s_orow = reinterpret_cast<int*>(sa0) + BM;
     if (!GATEUP) {
       __syncthreads();
       if (tid < BM) {
@@ -621,7 +658,7 @@ hipError_t launch_stream(const FfnArgs& a, hipStream_t st) {
   }
 }
 
-template <bool GATEUP, int BM, bool F8>
+template <bool GATEUP, int BM, bool F8, bool A32 = true>
 hipError_t launch_tile_bm(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipStream_t st) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;
   const int NT = ceil_div(a.ncols, HC);
@@ -630,7 +667,7 @@ hipError_t launch_tile_bm(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipSt
   long grid = (num_cu / 8) * 8;
   if (ub < grid) grid = ((ub + 7) / 8) * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
+  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8, A32>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
   return hipGetLastError();
 }
 
@@ -646,8 +683,20 @@ hipError_t launch_tile_bm(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipSt
 // 1.25 -> 1.39 ms on the Qwen3-235B shape).
 // a2: an optional single-group segment (a2.E == 1, a2.fixed_rows rows) run
 // in the same launch, with the tile height chosen for a.
+// Bytes of a segment's token matrix, or ~0 where its row count is not known.
+unsigned long long token_bytes(const FfnArgs& a) {
+  if (a.a_rows != nullptr && a.a_nrows <= 0) return ~0ull;
+  const long long rows = a.a_rows != nullptr ? a.a_nrows : a.rows_total;
+  return (unsigned long long)rows * (unsigned long long)a.K * 2ull;
+}
+
 template <bool GATEUP, bool F8>
-hipError_t launch_tile(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipStream_t st) {
+hipError_t launch_tile(const FfnArgs& a_in, const FfnArgs& a2_in, int num_cu, hipStream_t st) {
+  FfnArgs a = a_in, a2 = a2_in;
+  const unsigned long long tb = token_bytes(a), tb2 = a2.E > 0 ? token_bytes(a2) : 0;
+  if (tb > 0xFFFFFFFFull || tb2 > 0xFFFFFFFFull) return launch_tile_bm<GATEUP, 128, F8, false>(a, a2, num_cu, st);
+  a.a_bytes = (uint32_t)tb;
+  a2.a_bytes = (uint32_t)tb2;
   const double mean = (double)a.rows_total / (a.E > 0 ? a.E : 1);
   if (1.25 * mean <= 128.0) return launch_tile_bm<GATEUP, 128, F8>(a, a2, num_cu, st);
   if (1.25 * mean <= 192.0 || (!F8 && mean <= 640.0)) return launch_tile_bm<GATEUP, 192, F8>(a, a2, num_cu, st);

@@ -60,6 +60,10 @@ struct FfnArgs {
   // token row of the layer output: top-1 routing without shared experts
   // needs no combine)
   const int32_t* out_rows = nullptr;
+  // rows of `a` where a_rows is set (0: not known); a launcher sets a_bytes
+  // to the bytes of `a` when they fit 32-bit offsets
+  int a_nrows = 0;
+  uint32_t a_bytes = 0;
   // FP8 weights: if q0 is set, w0/w1 are unused and q0/q1 hold OCP E4M3
   // codes laid out like them; s0/s1 [E][ncols] are the float32 scales of
   // each output channel (weight = value(code) * scale)
