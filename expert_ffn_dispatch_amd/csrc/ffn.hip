@@ -752,18 +752,6 @@ hipError_t launch_tile_bm(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipSt
   return hipGetLastError();
 }
 
-// Tile height from the mean rows per group.  128 rows where 1.25x the mean
-// fits one such tile, 192 where it fits that.  With bf16 weights 192 rows
-// also up to a mean of 640: a group pads about half a tile on average (96
-// rows against 128), which outweighs the shorter tile's ~4% lower efficiency
-// per row until the groups are several tiles deep.  Measured: a 256-row tile
-// over 154-row groups wastes 40% of its MFMA work (DeepSeek-V2-shaped layer
-// 2.91 -> 2.63 ms with 192); bf16 Qwen3-235B-shaped groups (mean 512)
-// 3.47 -> 3.30 ms with 192; the expert-node share (mean 2048) is 1-2% faster
-// with 256; with FP8 weights the 192-row down launch was slower (about
-// 1.25 -> 1.39 ms on the Qwen3-235B shape).
-// a2: an optional single-group segment (a2.E == 1, a2.fixed_rows rows) run
-// in the same launch, with the tile height chosen for a.
 // Bytes of a segment's token matrix, or ~0 where its row count is not known.
 unsigned long long token_bytes(const FfnArgs& a) {
   if (a.a_rows != nullptr && a.a_nrows <= 0) return ~0ull;
@@ -771,6 +759,18 @@ unsigned long long token_bytes(const FfnArgs& a) {
   return (unsigned long long)rows * (unsigned long long)a.K * 2ull;
 }
 
+// Tile height from the mean rows per group.  128 rows where 1.25x the mean
+// fits one such tile, 192 where it fits that, and 192 also up to a mean of
+// 640: a group pads about half a tile on average (96 rows against 128),
+// which outweighs the shorter tile's lower efficiency per row until the
+// groups are several tiles deep (and 192-row tiles keep their weight rows
+// two stages ahead, which 256-row tiles have no LDS for).  Measured: a
+// 256-row tile over 154-row groups wastes 40% of its MFMA work (DeepSeek-V2-
+// shaped layer 2.91 -> 2.63 ms with 192); Qwen3-235B-shaped groups (mean 512)
+// 3.47 -> 3.30 ms with 192 (FP8 weights 3.15 -> 2.95 ms); the expert-node
+// share (mean 2048) is 1-2% faster with 256.
+// a2: an optional single-group segment (a2.E == 1, a2.fixed_rows rows) run
+// in the same launch, with the tile height chosen for a.
 template <bool GATEUP, bool F8>
 hipError_t launch_tile(const FfnArgs& a_in, const FfnArgs& a2_in, int num_cu, hipStream_t st) {
   FfnArgs a = a_in, a2 = a2_in;
@@ -780,7 +780,7 @@ hipError_t launch_tile(const FfnArgs& a_in, const FfnArgs& a2_in, int num_cu, hi
   a2.a_bytes = (uint32_t)tb2;
   const double mean = (double)a.rows_total / (a.E > 0 ? a.E : 1);
   if (1.25 * mean <= 128.0) return launch_tile_bm<GATEUP, 128, F8>(a, a2, num_cu, st);
-  if (1.25 * mean <= 192.0 || (!F8 && mean <= 640.0)) return launch_tile_bm<GATEUP, 192, F8>(a, a2, num_cu, st);
+  if (1.25 * mean <= 192.0 || mean <= 640.0) return launch_tile_bm<GATEUP, 192, F8>(a, a2, num_cu, st);
   return launch_tile_bm<GATEUP, 256, F8>(a, a2, num_cu, st);
 }
 

@@ -430,8 +430,9 @@ RoutePlan plan(int N, int M, int E) {
   int ks = ceil_div(1024, blocks);
   const int max_ks = ceil_div(total_steps, 16);     // slices of at least 512 k (128 per wave)
   if (ks > max_ks) ks = max_ks;
-  // partial scores are written and re-read once: keep them small
-  while (ks > 1 && (size_t)ks * N * p.EP * 4 > ((size_t)16 << 20)) --ks;
+  // partial scores are written and re-read once: keep them under 32 MB
+  // (16 MB cost the DeepSeek-V2-shaped router 2 us of its 64)
+  while (ks > 1 && (size_t)ks * N * p.EP * 4 > ((size_t)32 << 20)) --ks;
   if (ks < 1) ks = 1;
   p.steps = ceil_div(total_steps, ks);
   p.KS = ceil_div(total_steps, p.steps);
@@ -543,6 +544,8 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
     hipLaunchKernelGGL(router_topk_kernel<1>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
   else if (per <= 2)
     hipLaunchKernelGGL(router_topk_kernel<2>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
+  else if (per <= 3)
+    hipLaunchKernelGGL(router_topk_kernel<3>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
   else
     hipLaunchKernelGGL(router_topk_kernel<4>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
   return hipGetLastError();
