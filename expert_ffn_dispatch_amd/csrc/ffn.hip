@@ -399,15 +399,19 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   // into one buffer do not touch the reads of another (as parts of one array
   // it waits for the loads before every read).
   constexpr int NB = BM == 256 ? 2 : 3;
+  // (three token buffers, with two or three weight buffers: 5% slower with
+  // bf16 weights, within 1% with FP8)
+  constexpr int NA = 2;
   // TR: accumulators hold D[weight row][token row] (operands swapped), so
-  // that the epilogue stores four consecutive columns per lane; bf16 down
-  // with 256-row tiles keeps D[token row][weight row] and 2-byte stores,
-  // which measured faster there (expert-node share down 519 -> 474 us) while
-  // the swapped form is faster or equal everywhere else (FP8 Qwen3-235B-shaped
-  // layer 3.37 -> 3.19 ms).
-  constexpr bool TR = GATEUP || F8 || BM < 256;
+  // that the epilogue stores four consecutive columns per lane; down with
+  // 256-row tiles keeps D[token row][weight row] and 2-byte stores, which
+  // measured faster there (expert-node share down 519 -> 474 us with bf16
+  // weights) while the swapped form is faster or equal everywhere else (FP8
+  // Qwen3-235B-shaped layer 3.37 -> 3.19 ms).
+  constexpr bool TR = GATEUP || BM < 256;
   __shared__ __align__(16) uint16_t sa0[STA];
   __shared__ __align__(16) uint16_t sa1[STA];
+  __shared__ __align__(16) uint16_t sa2[NA == 3 ? STA : 8];
   __shared__ __align__(16) uint16_t sb0[STB];
   __shared__ __align__(16) uint16_t sb1[STB];
   __shared__ __align__(16) uint16_t sb2[NB == 3 ? STB : 8];
@@ -544,9 +548,16 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     __syncthreads();
     // issue order: weights of stage 0, tokens of stage 0 (three weight
     // buffers: then the weights of stage 1)
-    MOE_DMA_B(sb0, 0)
-    MOE_DMA_A(sa0, 0)
-    if (NB == 3) { MOE_DMA_B(sb1, min(1, KT - 1)) }
+    if constexpr (NB == 3 && NA == 2) {
+      MOE_DMA_B(sb0, 0)
+      MOE_DMA_A(sa0, 0)
+      MOE_DMA_B(sb1, min(1, KT - 1))
+    } else {
+      MOE_DMA_A(sa0, 0)
+      MOE_DMA_B(sb0, 0)
+      if (NA == 3) { MOE_DMA_A(sa1, min(1, KT - 1)) }
+      if (NB == 3) { MOE_DMA_B(sb1, min(1, KT - 1)) }
+    }
 
     // One stage: wait for this wave's loads of stage KT_ (with three weight
     // buffers the weights of stage KT_+1, issued last, may stay in flight),
@@ -560,10 +571,15 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     // sinks them to the end of the step, where they overlap nothing).
 #define MOE_TSTEP(ABUF, NABUF, BBUF, NBBUF, KT_)                                                   \
   {                                                                                                \
-    MOE_WAIT_VM(NB == 3 ? BI : 0);                                                                 \
+    MOE_WAIT_VM((NA == 3 ? AI : 0) + (NB == 3 ? BI : 0));                                         \
     __builtin_amdgcn_s_barrier();                                                                  \
-    MOE_DMA_A(NABUF, min((KT_) + 1, KT - 1))                                                       \
-    MOE_DMA_B(NBBUF, min((KT_) + NB - 1, KT - 1))                                                  \
+    if constexpr (NA == 3 && NB == 2) {                                                            \
+      MOE_DMA_B(NBBUF, min((KT_) + 1, KT - 1))                                                     \
+      MOE_DMA_A(NABUF, min((KT_) + 2, KT - 1))                                                     \
+    } else {                                                                                       \
+      MOE_DMA_A(NABUF, min((KT_) + NA - 1, KT - 1))                                                \
+      MOE_DMA_B(NBBUF, min((KT_) + NB - 1, KT - 1))                                                \
+    }                                                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                             \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                                \
       u32x4_t af[FMW], bf[2];                                                                      \
@@ -588,27 +604,33 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     // buffer kt % 2 and weight buffer kt % NB, a pattern of period 2 or 6;
     // the remainder continues it step by step
     int kt = 0;
-    if constexpr (NB == 2) {
+#define MOE_A(I) ((I) % NA == 0 ? sa0 : (I) % NA == 1 ? sa1 : sa2)
+#define MOE_B(I) ((I) % NB == 0 ? sb0 : (I) % NB == 1 ? sb1 : sb2)
+#define MOE_USTEP(U, KT_) MOE_TSTEP(MOE_A(U), MOE_A((U) + NA - 1), MOE_B(U), MOE_B((U) + NB - 1), KT_)
+    if constexpr (NA == 2 && NB == 2) {
       for (; kt + 1 < KT; kt += 2) {
-        MOE_TSTEP(sa0, sa1, sb0, sb1, kt)
-        MOE_TSTEP(sa1, sa0, sb1, sb0, kt + 1)
+        MOE_USTEP(0, kt)
+        MOE_USTEP(1, kt + 1)
       }
-      if (kt < KT) MOE_TSTEP(sa0, sa1, sb0, sb1, kt)
+      if (kt < KT) MOE_USTEP(0, kt)
     } else {
       for (; kt + 5 < KT; kt += 6) {
-        MOE_TSTEP(sa0, sa1, sb0, sb2, kt)
-        MOE_TSTEP(sa1, sa0, sb1, sb0, kt + 1)
-        MOE_TSTEP(sa0, sa1, sb2, sb1, kt + 2)
-        MOE_TSTEP(sa1, sa0, sb0, sb2, kt + 3)
-        MOE_TSTEP(sa0, sa1, sb1, sb0, kt + 4)
-        MOE_TSTEP(sa1, sa0, sb2, sb1, kt + 5)
+        MOE_USTEP(0, kt)
+        MOE_USTEP(1, kt + 1)
+        MOE_USTEP(2, kt + 2)
+        MOE_USTEP(3, kt + 3)
+        MOE_USTEP(4, kt + 4)
+        MOE_USTEP(5, kt + 5)
       }
-      if (kt < KT) MOE_TSTEP(sa0, sa1, sb0, sb2, kt)
-      if (kt + 1 < KT) MOE_TSTEP(sa1, sa0, sb1, sb0, kt + 1)
-      if (kt + 2 < KT) MOE_TSTEP(sa0, sa1, sb2, sb1, kt + 2)
-      if (kt + 3 < KT) MOE_TSTEP(sa1, sa0, sb0, sb2, kt + 3)
-      if (kt + 4 < KT) MOE_TSTEP(sa0, sa1, sb1, sb0, kt + 4)
+      if (kt < KT) MOE_USTEP(0, kt)
+      if (kt + 1 < KT) MOE_USTEP(1, kt + 1)
+      if (kt + 2 < KT) MOE_USTEP(2, kt + 2)
+      if (kt + 3 < KT) MOE_USTEP(3, kt + 3)
+      if (kt + 4 < KT) MOE_USTEP(4, kt + 4)
     }
+#undef MOE_USTEP
+#undef MOE_A
+#undef MOE_B
 #undef MOE_TSTEP
 #undef MOE_DMA_A
 #undef MOE_DMA_B
@@ -626,6 +648,15 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
         s_scale[tid] = (pa.row_scale && tid < nrows) ? pa.row_scale[row0 + tid] : 1.f;
         s_orow[tid] = (pa.out_rows && tid < nrows) ? pa.out_rows[row0 + tid] : row0 + tid;
       }
+      // FP8: the per-channel scales of this lane's two columns
+      float wsc[2] = {1.f, 1.f};
+      if constexpr (F8) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = col0 + wn * 64 + 32 * j + fr;
+          if (col < ncols) wsc[j] = pa.s0[(size_t)e * ncols + col];
+        }
+      }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < FMW; ++i) {
@@ -640,7 +671,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const int col = col0 + wn * 64 + 32 * j + fr;
-              if (col < ncols) orow[col] = f32_to_bf16(acc[i][j][4 * b + q] * sc);
+              if (col < ncols) orow[col] = f32_to_bf16(acc[i][j][4 * b + q] * wsc[j] * sc);
             }
           }
         }
