@@ -679,6 +679,46 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       continue;
     }
 
+    if constexpr (TR && !GATEUP && !F8) {
+      // Down, bf16: each wave's (BM/2) x 64 output block goes through LDS so
+      // that the stores write whole 128-byte row segments, eight rows per
+      // instruction.  Stored straight from the swapped layout (16 bytes per
+      // row per instruction, over 32 rows) the output reached HBM as about
+      // 1.8x its bytes.  A wave's block lies in a stage buffer that every
+      // wave has finished reading; 16-byte chunk c of row r sits at
+      // c ^ (r & 7), so neither the writes nor the reads conflict.
+      constexpr int RB = BM / 2;
+      __syncthreads();
+      uint16_t* blk = (wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1) + (wave & 1) * RB * 64;
+#pragma unroll
+      for (int i = 0; i < FMW; ++i) {
+        const int r = 32 * i + fr;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const f32x16_t& a0 = acc[i][j];
+            const uint2 v = make_uint2(pack_bf16x2(a0[4 * b] * rsc[i], a0[4 * b + 1] * rsc[i]),
+                                       pack_bf16x2(a0[4 * b + 2] * rsc[i], a0[4 * b + 3] * rsc[i]));
+            *reinterpret_cast<uint2*>(blk + r * 64 + (((4 * j + b) ^ (r & 7)) << 3) + 4 * fg) = v;
+          }
+      }
+      __builtin_amdgcn_wave_barrier();         // a wave's LDS operations complete in order
+      const int c = col0 + wn * 64;
+      if (c < ncols) {
+        const int ch = lane & 7;
+#pragma unroll
+        for (int t = 0; t < RB / 8; ++t) {
+          const int r = 8 * t + (lane >> 3);
+          const uint4 v = *reinterpret_cast<const uint4*>(blk + r * 64 + ((ch ^ (r & 7)) << 3));
+          const int orow = __shfl(orow_i[t >> 2], r & 31);
+          if (wm * RB + r < nrows)
+            *reinterpret_cast<uint4*>(pa.out + (size_t)orow * ncols + c + ch * 8) = v;
+        }
+      }
+      continue;
+    }
+
     // Epilogue.  acc[i][j] holds D[weight row][token row] of a 32 x 32 block:
     // this lane's token row is 32 i + (lane & 31) of the wave's half, and
     // element 4 b + q is output column 8 b + 4 (lane >> 5) + q of block j, so
