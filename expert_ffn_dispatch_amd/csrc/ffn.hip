@@ -402,13 +402,14 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   // (three token buffers, with two or three weight buffers: 5% slower with
   // bf16 weights, within 1% with FP8)
   constexpr int NA = 2;
-  // TR: accumulators hold D[weight row][token row] (operands swapped), so
-  // that the epilogue stores four consecutive columns per lane; down with
-  // 256-row tiles keeps D[token row][weight row] and 2-byte stores, which
-  // measured faster there (expert-node share down 519 -> 474 us with bf16
-  // weights) while the swapped form is faster or equal everywhere else (FP8
-  // Qwen3-235B-shaped layer 3.37 -> 3.19 ms).
-  constexpr bool TR = GATEUP || BM < 256;
+  // TR: accumulators hold D[weight row][token row] (operands swapped): the
+  // epilogue then stores four consecutive columns per lane (FP8 Qwen3-235B-
+  // shaped layer 3.37 -> 3.19 ms), and bf16 down stages its output through
+  // LDS as whole row segments.  FP8 down with 256-row tiles keeps
+  // D[token row][weight row] and 2-byte stores, which measured faster there
+  // than the swapped form with direct stores (expert-node share FP8 layer
+  // 1.33 -> 1.30 ms).
+  constexpr bool TR = GATEUP || BM < 256 || !F8;
   __shared__ __align__(16) uint16_t sa0[STA];
   __shared__ __align__(16) uint16_t sa1[STA];
   __shared__ __align__(16) uint16_t sa2[NA == 3 ? STA : 8];
