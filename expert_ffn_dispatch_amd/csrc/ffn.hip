@@ -720,6 +720,50 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       continue;
     }
 
+    if constexpr (TR && !GATEUP && F8) {
+      // Down, FP8 weights: the same through LDS, one 32-row block at a time
+      // (the weight buffers are too small for whole wave blocks), each wave
+      // in a 4 KB slot of the token buffers.
+      constexpr int RB = BM / 2;
+      __syncthreads();
+      uint16_t* blk = (wave < 4 ? sa0 : sa1) + (wave & 3) * 32 * 64;
+      const int c = col0 + wn * 64;
+      float4 sc4[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          sc4[j][b] = c < ncols ? *reinterpret_cast<const float4*>(pa.s0 + (size_t)e * ncols + c + 32 * j + 8 * b + 4 * fg)
+                                : make_float4(1.f, 1.f, 1.f, 1.f);
+      const int ch = lane & 7;
+#pragma unroll
+      for (int i = 0; i < FMW; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const f32x16_t& a0 = acc[i][j];
+            const float4 g = sc4[j][b];
+            const uint2 v = make_uint2(pack_bf16x2(a0[4 * b] * g.x * rsc[i], a0[4 * b + 1] * g.y * rsc[i]),
+                                       pack_bf16x2(a0[4 * b + 2] * g.z * rsc[i], a0[4 * b + 3] * g.w * rsc[i]));
+            *reinterpret_cast<uint2*>(blk + fr * 64 + (((4 * j + b) ^ (fr & 7)) << 3) + 4 * fg) = v;
+          }
+        __builtin_amdgcn_wave_barrier();       // a wave's LDS operations complete in order
+        if (c < ncols) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = 8 * t + (lane >> 3);
+            const uint4 v = *reinterpret_cast<const uint4*>(blk + r * 64 + ((ch ^ (r & 7)) << 3));
+            const int orow = __shfl(orow_i[i], r);
+            if (wm * RB + 32 * i + r < nrows)
+              *reinterpret_cast<uint4*>(pa.out + (size_t)orow * ncols + c + ch * 8) = v;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      continue;
+    }
+
     // Epilogue.  acc[i][j] holds D[weight row][token row] of a 32 x 32 block:
     // this lane's token row is 32 i + (lane & 31) of the wave's half, and
     // element 4 b + q is output column 8 b + 4 (lane >> 5) + q of block j, so
