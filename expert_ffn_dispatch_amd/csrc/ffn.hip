@@ -402,14 +402,13 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   // (three token buffers, with two or three weight buffers: 5% slower with
   // bf16 weights, within 1% with FP8)
   constexpr int NA = 2;
-  // TR: accumulators hold D[weight row][token row] (operands swapped): the
-  // epilogue then stores four consecutive columns per lane (FP8 Qwen3-235B-
-  // shaped layer 3.37 -> 3.19 ms), and bf16 down stages its output through
-  // LDS as whole row segments.  FP8 down with 256-row tiles keeps
-  // D[token row][weight row] and 2-byte stores, which measured faster there
-  // than the swapped form with direct stores (expert-node share FP8 layer
-  // 1.33 -> 1.30 ms).
-  constexpr bool TR = GATEUP || BM < 256 || !F8;
+  // The MFMA takes the weight fragment as its first operand, so the
+  // accumulators hold D[weight row][token row]: each lane ends with one
+  // token row and four consecutive output columns per 32 x 32 block.  The
+  // epilogue then stores four columns per lane (gate+up) or stages down's
+  // output through LDS as whole row segments (FP8 Qwen3-235B-shaped layer
+  // 3.37 -> 3.19 ms for the swap, 2.92 -> 2.72 ms for the staging; with
+  // D[token row][weight row] lanes would hold columns and store 2 bytes).
   __shared__ __align__(16) uint16_t sa0[STA];
   __shared__ __align__(16) uint16_t sa1[STA];
   __shared__ __align__(16) uint16_t sa2[NA == 3 ? STA : 8];
@@ -516,7 +515,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     // contraction
     float rsc[FMW];
     int orow_i[FMW];
-    if constexpr (TR && !GATEUP) {
+    if constexpr (!GATEUP) {
 #pragma unroll
       for (int i = 0; i < FMW; ++i) {
         const int row = wm * (BM / 2) + 32 * i + fr;
@@ -596,7 +595,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       }                                                                                            \
       _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
           _Pragma("unroll") for (int j = 0; j < 2; ++j)                                            \
-              acc[i][j] = TR ? mfma32(bf[j], af[i], acc[i][j]) : mfma32(af[i], bf[j], acc[i][j]);  \
+              acc[i][j] = mfma32(bf[j], af[i], acc[i][j]);                                          \
     }                                                                                              \
     MOE_WAIT_LGKM0();                                                                              \
   }
@@ -637,50 +636,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 #undef MOE_DMA_B
     MOE_WAIT_VM(0);
 
-    if constexpr (!TR) {
-      // acc[i][j] holds D[token row][weight row] of a 32 x 32 block: this
-      // lane's column is 32 j + (lane & 31) of the wave's 64, its rows
-      // 32 i + 8 b + 4 (lane >> 5) + q.  Row scales and output rows through
-      // LDS (the first token buffer is free once every wave has finished).
-      float* s_scale = reinterpret_cast<float*>(sa0);
-      int* s_orow = reinterpret_cast<int*>(sa0) + BM;
-      __syncthreads();
-      if (tid < BM) {
-        s_scale[tid] = (pa.row_scale && tid < nrows) ? pa.row_scale[row0 + tid] : 1.f;
-        s_orow[tid] = (pa.out_rows && tid < nrows) ? pa.out_rows[row0 + tid] : row0 + tid;
-      }
-      // FP8: the per-channel scales of this lane's two columns
-      float wsc[2] = {1.f, 1.f};
-      if constexpr (F8) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = col0 + wn * 64 + 32 * j + fr;
-          if (col < ncols) wsc[j] = pa.s0[(size_t)e * ncols + col];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < FMW; ++i) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = wm * (BM / 2) + 32 * i + 8 * b + 4 * fg + q;
-            if (row >= nrows) continue;
-            uint16_t* orow = pa.out + (size_t)s_orow[row] * ncols;
-            const float sc = s_scale[row];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int col = col0 + wn * 64 + 32 * j + fr;
-              if (col < ncols) orow[col] = f32_to_bf16(acc[i][j][4 * b + q] * wsc[j] * sc);
-            }
-          }
-        }
-      }
-      continue;
-    }
-
-    if constexpr (TR && !GATEUP && !F8) {
+    if constexpr (!GATEUP && !F8) {
       // Down, bf16: each wave's (BM/2) x 64 output block goes through LDS so
       // that the stores write whole 128-byte row segments, eight rows per
       // instruction.  Stored straight from the swapped layout (16 bytes per
@@ -720,7 +676,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       continue;
     }
 
-    if constexpr (TR && !GATEUP && F8) {
+    if constexpr (!GATEUP && F8) {
       // Down, FP8 weights: the same through LDS, one 32-row block at a time
       // (the weight buffers are too small for whole wave blocks), each wave
       // in a 4 KB slot of the token buffers.
@@ -764,45 +720,35 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       continue;
     }
 
-    // Epilogue.  acc[i][j] holds D[weight row][token row] of a 32 x 32 block:
-    // this lane's token row is 32 i + (lane & 31) of the wave's half, and
-    // element 4 b + q is output column 8 b + 4 (lane >> 5) + q of block j, so
-    // every lane stores four consecutive bf16 columns (8 bytes) at a time.
-    // Column groups of four lie wholly inside or outside ncols (a multiple of
-    // 64).  FP8: the per-channel scales of those columns, four at a time.
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    // Gate+up.  acc[i][0] and acc[i][1] hold the gate and up sums of the same
+    // 32 h columns: this lane's token row is 32 i + (lane & 31) of the wave's
+    // half, and element 4 b + q is column 8 b + 4 (lane >> 5) + q, so every
+    // lane stores four consecutive h columns (8 bytes) at a time.  Column
+    // groups of four lie wholly inside or outside ncols (a multiple of 64).
+    // FP8: the per-channel scales of those columns, four at a time.
+    if constexpr (GATEUP) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int c = GATEUP ? col0 + wn * 32 + 8 * b + 4 * fg : col0 + wn * 64 + 32 * j + 8 * b + 4 * fg;
-        if (GATEUP && j == 1) continue;        // gate and up columns are stored together
+        const int c = col0 + wn * 32 + 8 * b + 4 * fg;
         if (c >= ncols) continue;
         float4 sg = make_float4(1.f, 1.f, 1.f, 1.f), su = sg;
         if constexpr (F8) {
           sg = *reinterpret_cast<const float4*>(pa.s0 + (size_t)e * ncols + c);
-          if (GATEUP) su = *reinterpret_cast<const float4*>(pa.s1 + (size_t)e * ncols + c);
+          su = *reinterpret_cast<const float4*>(pa.s1 + (size_t)e * ncols + c);
         }
+        const float gs[4] = {sg.x, sg.y, sg.z, sg.w}, us[4] = {su.x, su.y, su.z, su.w};
 #pragma unroll
         for (int i = 0; i < FMW; ++i) {
           const int row = wm * (BM / 2) + 32 * i + fr;
           if (row >= nrows) continue;
-          const f32x16_t& a0 = acc[i][GATEUP ? 0 : j];
           float v[4];
-          if constexpr (GATEUP) {
-            const f32x16_t& a1 = acc[i][1];
-            const float gs[4] = {sg.x, sg.y, sg.z, sg.w}, us[4] = {su.x, su.y, su.z, su.w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float g = a0[4 * b + q] * gs[q], u = a1[4 * b + q] * us[q];
-              v[q] = g / (1.f + __expf(-g)) * u;
-            }
-          } else {
-            const float gs[4] = {sg.x, sg.y, sg.z, sg.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = a0[4 * b + q] * gs[q] * rsc[i];
+          for (int q = 0; q < 4; ++q) {
+            const float g = acc[i][0][4 * b + q] * gs[q], u = acc[i][1][4 * b + q] * us[q];
+            v[q] = g / (1.f + __expf(-g)) * u;
           }
-          const size_t orow = GATEUP ? (size_t)(row0 + row) : (size_t)orow_i[i];
-          *reinterpret_cast<uint2*>(pa.out + orow * ncols + c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          *reinterpret_cast<uint2*>(pa.out + (size_t)(row0 + row) * ncols + c) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       }
     }
