@@ -636,50 +636,15 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 #undef MOE_DMA_B
     MOE_WAIT_VM(0);
 
-    if constexpr (!GATEUP && !F8) {
-      // Down, bf16: each wave's (BM/2) x 64 output block goes through LDS so
-      // that the stores write whole 128-byte row segments, eight rows per
-      // instruction.  Stored straight from the swapped layout (16 bytes per
-      // row per instruction, over 32 rows) the output reached HBM as about
-      // 1.8x its bytes.  A wave's block lies in a stage buffer that every
-      // wave has finished reading; 16-byte chunk c of row r sits at
-      // c ^ (r & 7), so neither the writes nor the reads conflict.
-      constexpr int RB = BM / 2;
-      __syncthreads();
-      uint16_t* blk = (wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1) + (wave & 1) * RB * 64;
-#pragma unroll
-      for (int i = 0; i < FMW; ++i) {
-        const int r = 32 * i + fr;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const f32x16_t& a0 = acc[i][j];
-            const uint2 v = make_uint2(pack_bf16x2(a0[4 * b] * rsc[i], a0[4 * b + 1] * rsc[i]),
-                                       pack_bf16x2(a0[4 * b + 2] * rsc[i], a0[4 * b + 3] * rsc[i]));
-            *reinterpret_cast<uint2*>(blk + r * 64 + (((4 * j + b) ^ (r & 7)) << 3) + 4 * fg) = v;
-          }
-      }
-      __builtin_amdgcn_wave_barrier();         // a wave's LDS operations complete in order
-      const int c = col0 + wn * 64;
-      if (c < ncols) {
-        const int ch = lane & 7;
-#pragma unroll
-        for (int t = 0; t < RB / 8; ++t) {
-          const int r = 8 * t + (lane >> 3);
-          const uint4 v = *reinterpret_cast<const uint4*>(blk + r * 64 + ((ch ^ (r & 7)) << 3));
-          const int orow = __shfl(orow_i[t >> 2], r & 31);
-          if (wm * RB + r < nrows)
-            *reinterpret_cast<uint4*>(pa.out + (size_t)orow * ncols + c + ch * 8) = v;
-        }
-      }
-      continue;
-    }
-
-    if constexpr (!GATEUP && F8) {
-      // Down, FP8 weights: the same through LDS, one 32-row block at a time
-      // (the weight buffers are too small for whole wave blocks), each wave
-      // in a 4 KB slot of the token buffers.
+    if constexpr (!GATEUP) {
+      // Down: the output goes through LDS so that the stores write whole
+      // 128-byte row segments, eight rows per instruction.  Stored straight
+      // from the accumulators (16 bytes per row per instruction, over 32
+      // rows) it reached HBM as about 1.8x its bytes.  Each wave stages one
+      // 32 x 64 block at a time in a 4 KB slot of the token buffers, which
+      // every wave has finished reading; 16-byte chunk c of row r sits at
+      // c ^ (r & 7), so neither the writes nor the reads conflict.  FP8:
+      // the per-channel scales of this lane's columns, four at a time.
       constexpr int RB = BM / 2;
       __syncthreads();
       uint16_t* blk = (wave < 4 ? sa0 : sa1) + (wave & 3) * 32 * 64;
@@ -689,7 +654,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          sc4[j][b] = c < ncols ? *reinterpret_cast<const float4*>(pa.s0 + (size_t)e * ncols + c + 32 * j + 8 * b + 4 * fg)
+          sc4[j][b] = (F8 && c < ncols) ? *reinterpret_cast<const float4*>(pa.s0 + (size_t)e * ncols + c + 32 * j + 8 * b + 4 * fg)
                                 : make_float4(1.f, 1.f, 1.f, 1.f);
       const int ch = lane & 7;
 #pragma unroll
