@@ -254,13 +254,17 @@ def token_outputs(inp: Dict[str, np.ndarray], topk_ids: np.ndarray, topk_weights
     tokens = np.asarray(tokens, dtype=np.int64)
     x = inp["x"][tokens]
     X = bf16_to_f64(x)
-    ids = np.asarray(topk_ids)[tokens]
-    w = np.asarray(topk_weights, np.float64)[tokens]
+    ids_all = np.asarray(topk_ids)
+    ids = ids_all.reshape(ids_all.shape[0], -1)[tokens]
+    w = np.asarray(topk_weights, np.float64).reshape(ids_all.shape[0], -1)[tokens]
     out = np.zeros((len(tokens), X.shape[1]), np.float64)
-    for e in np.unique(ids):
-        rows, slots = np.nonzero(ids == e)
-        Y, _ = swiglu(X[rows], inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
-        out[rows] += w[rows, slots][:, None] * Y
+    # slot by slot, then expert by expert: inside one slot a token appears
+    # once, so the row updates below never collide
+    for j in range(ids.shape[1]):
+        for e in np.unique(ids[:, j]):
+            rows = np.nonzero(ids[:, j] == e)[0]
+            Y, _ = swiglu(X[rows], inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
+            out[rows] += w[rows, j][:, None] * Y
     if S > 0:
         out += shared_experts(x, inp["ws_gate"], inp["ws_up"], inp["ws_down"], S, Hs)
     return out

@@ -62,6 +62,70 @@ def test_brute_force(case):
 
 
 # --------------------------------------------------------------------------
+# the per-token form and the expert-node share
+# --------------------------------------------------------------------------
+
+def check_token_outputs(case, seed=1):
+    """token_outputs (the per-token definition that full-size GPU runs are
+    checked against) equals brute force fed the same routing, on every token
+    and on a scrambled subset with a repeated token; and equals the batched
+    layer's combine on every token."""
+    N, M, E, k, H, S, Hs, _ = case
+    inp = _small(case, seed)
+    o = O.moe_layer(inp, k, S, Hs)
+    ids, w = o["topk_ids"], o["topk_weights"]
+    b = brute.layer(inp, k, S, Hs, ids_in=ids, w_in=w)
+    scale = max(1.0, np.abs(b["out"]).max())
+    t = O.token_outputs(inp, ids, w, np.arange(N), S, Hs)
+    np.testing.assert_allclose(t, b["out"], rtol=1e-11, atol=1e-12 * scale)
+    np.testing.assert_allclose(t, o["out"], rtol=1e-11, atol=1e-12 * scale)
+    sub = np.array([N - 1, 0, N // 2, N - 1])
+    t2 = O.token_outputs(inp, ids, w, sub, S, Hs)
+    np.testing.assert_allclose(t2, b["out"][sub], rtol=1e-11, atol=1e-12 * scale)
+    # arbitrary routing (not the router's): distinct random experts per
+    # token, weights of either sign that do not sum to one
+    rng = np.random.default_rng(seed + 17)
+    ids_r = np.stack([rng.permutation(E)[:k] for _ in range(N)]).astype(np.int32)
+    w_r = rng.uniform(-1.5, 2.0, size=(N, k)).astype(np.float32)
+    br = brute.layer(inp, k, S, Hs, ids_in=ids_r, w_in=w_r)
+    tr = O.token_outputs(inp, ids_r, w_r, np.arange(N), S, Hs)
+    np.testing.assert_allclose(tr, br["out"], rtol=1e-11, atol=1e-12 * max(1.0, np.abs(br["out"]).max()))
+
+
+def check_expert_node(N=23, M=16, E=6, H=8, seed=3):
+    """expert_node: pre-routed rows (k = 1) with arbitrary weights, some
+    experts empty; equals brute force with k = 1 (which scatters each row's
+    weighted output back to its arrival position), counts and permutation
+    included."""
+    inp = gen.random_small(N, M, E, 1, H, seed=seed, std=0.3)
+    rng = np.random.default_rng(seed)
+    used = np.array([1, 2, 4])                     # the other experts get no rows
+    ids = rng.choice(used, size=(N, 1)).astype(np.int32)
+    ids[0, 0] = 4
+    w = rng.uniform(-2.0, 3.0, size=(N, 1)).astype(np.float32)
+    r = O.expert_node(inp["x"], ids, w, inp["w_gate"], inp["w_up"], inp["w_down"])
+    b = brute.layer(inp, 1, ids_in=ids, w_in=w)
+    assert np.array_equal(r["expert_counts"], np.asarray(b["counts"]))
+    empty = np.setdiff1d(np.arange(E), used)
+    assert empty.size > 0 and r["expert_counts"][empty].sum() == 0
+    assert np.array_equal(r["sorted_to_assign"], np.asarray(b["sorted_to_assign"]))
+    np.testing.assert_allclose(r["out"], b["out"], rtol=1e-11, atol=1e-12 * max(1.0, np.abs(b["out"]).max()))
+    # and the per-token form agrees with it (k = 1)
+    t = O.token_outputs(inp, ids, w, np.arange(N))
+    np.testing.assert_allclose(t, b["out"], rtol=1e-11, atol=1e-12 * max(1.0, np.abs(b["out"]).max()))
+
+
+@pytest.mark.parametrize("case", SMALL_CASES)
+def test_token_outputs(case):
+    check_token_outputs(case)
+
+
+def test_expert_node():
+    check_expert_node()
+    check_expert_node(N=1, E=5, seed=4)
+
+
+# --------------------------------------------------------------------------
 # closed forms
 # --------------------------------------------------------------------------
 
@@ -225,6 +289,8 @@ def _all_pins():
     w = configs.TINY
     d = gen.generate(w)
     check_invariants(O.moe_layer(d, w.k), w.N, w.E, w.k)
+    check_token_outputs(SMALL_CASES[2])
+    check_expert_node()
 
 
 def _mut_tie_high(p, k):
@@ -283,7 +349,18 @@ def _mut_no_softmax_max(logits):
     return z / z.sum(axis=1, keepdims=True) * np.float32(1.0 + 1e-3)
 
 
-ORIG = {name: getattr(O, name) for name in ("topk", "swiglu", "dispatch", "combine", "gather", "softmax32")}
+def _mut_token_outputs_slot0_weight(inp, topk_ids, topk_weights, tokens, S=0, Hs=0):
+    w = np.array(topk_weights, np.float32, copy=True)
+    w[:] = w[:, :1]
+    return ORIG["token_outputs"](inp, topk_ids, w, tokens, S, Hs)
+
+
+def _mut_expert_node_no_weight(x, topk_ids, topk_weights, w_gate, w_up, w_down):
+    return ORIG["expert_node"](x, topk_ids, np.ones_like(np.asarray(topk_weights)), w_gate, w_up, w_down)
+
+
+ORIG = {name: getattr(O, name) for name in ("topk", "swiglu", "dispatch", "combine", "gather", "softmax32",
+                                            "token_outputs", "expert_node")}
 
 MUTANTS = [
     ("topk", _mut_tie_high),
@@ -295,6 +372,8 @@ MUTANTS = [
     ("combine", _mut_drop_shared),
     ("gather", _mut_gather_mod),
     ("softmax32", _mut_no_softmax_max),
+    ("token_outputs", _mut_token_outputs_slot0_weight),
+    ("expert_node", _mut_expert_node_no_weight),
 ]
 
 
