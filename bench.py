@@ -2,18 +2,24 @@
 """Throughput of one MoE FFN layer (moe_layer) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--tokens N]
-                    [--fp8 | --micro-batches M | --cost-model]
+                    [--no-flush] [--fp8 | --micro-batches M | --cost-model]
 
 A step is one moe_layer call over one batch of synthetic, seeded input that is
 already resident in HBM: router -> top-k -> dispatch/permutation -> grouped
 SwiGLU (gate+up, down) -> shared experts -> combine.  The default workload is
-the Mixtral-8x22B-shaped decode batch (N=156 tokens, M=6144, E=8, top-2,
-H=16384), the batch the MegaScale-Infer summary uses to show 39 rows per
-expert.  Prints ONE JSON line: tokens/s over K timed back-to-back steps, the
-per-stage times from events recorded inside the layer during K further
-(instrumented) steps, the roofline of the dominant kernel (the gate+up GEMM,
-HBM-bound at this batch) and the oracle timed on the host cores as a CPU
-baseline.
+the Qwen3-235B-shaped skewed layer (N=8192 tokens, M=4096, E=128, top-8,
+H=1536, a Zipf-shaped router bias that gives the hottest expert 4x the mean
+load), the largest workload that fits one GPU and the one where the expert
+GEMMs are bound by the matrix cores.  Other workloads: --workload tiny,
+mixtral, dsv2, qwen30 (with --tokens), qwen235_node.
+
+Timing: W untimed warm-up calls, then K timed calls; before each call a 1 GiB
+buffer is read (outside the events), so that L2 and the Infinity Cache hold
+nothing of the layer, and each call is bracketed by two events on the layer's
+stream.  The step time is the median call; p10/p90 are reported beside it.
+A further K calls record events at the layer's stage boundaries; the gate+up
+launch's mean time from them gives the dominant kernel's roofline.  The
+oracle is timed on the host cores as the CPU baseline.  Prints ONE JSON line.
 """
 import argparse
 import json
@@ -75,25 +81,43 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def host_cores() -> int:
+    """Cores this process may run on (its affinity mask), capped by
+    OMP_NUM_THREADS where that is set (the host's share of cores per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
 def cpu_baseline(w, d, budget_s: float = 20.0, max_runs: int = 5):
-    """The oracle on the host cores over the same inputs: up to five runs of
-    the whole layer while they fit in about 20 s, median reported."""
+    """The oracle on the host cores over the same inputs: runs of the whole
+    layer while they fit in about 20 s (at least one, at most five), median
+    reported.  The BLAS pool is limited to the cores the process may use, and
+    that count is reported."""
     import threadpoolctl
     from oracle import moe_oracle as O
+    cores = host_cores()
     times = []
-    while len(times) < max_runs and sum(times) < budget_s:
-        t0 = time.perf_counter()
-        if w.pre_routed:
-            O.expert_node(d["x"], d["topk_ids"], d["topk_weights"], d["w_gate"], d["w_up"], d["w_down"])
-        else:
-            O.moe_layer(d, w.k, w.S, w.Hs)
-        times.append(time.perf_counter() - t0)
+    with threadpoolctl.threadpool_limits(limits=cores):
+        while len(times) < max_runs and sum(times) < budget_s:
+            t0 = time.perf_counter()
+            if w.pre_routed:
+                O.expert_node(d["x"], d["topk_ids"], d["topk_weights"], d["w_gate"], d["w_up"], d["w_down"])
+            else:
+                O.moe_layer(d, w.k, w.S, w.Hs)
+            times.append(time.perf_counter() - t0)
+        used = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
     dt = float(np.median(times))
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    return {"value": w.N / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": w.N / dt, "unit": "tokens/s", "cores": int(min(used, cores)), "kind": "oracle",
             "cpu_model": _cpu_model(), "runs": len(times),
             "sample": f"the whole {w.title} layer (N={w.N}) through the CPU oracle (float64 expert math, "
-                      f"float32 routing), median of {len(times)} runs: {dt:.2f} s"}
+                      f"float32 routing), {'median of ' + str(len(times)) + ' runs' if len(times) > 1 else 'one run'}"
+                      f": {dt:.2f} s"}
 
 
 def cost_model(args) -> int:
@@ -171,17 +195,18 @@ def cost_model(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen235")
     ap.add_argument("--tokens", type=int, default=None, help="token count for the decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30,
                     help="size of the plain device copy timed after the layer (0 = skip); its GB/s is "
                          "the practical bandwidth ceiling and its counters scale FETCH_SIZE/WRITE_SIZE")
-    ap.add_argument("--flush", action="store_true",
-                    help="read a 1 GiB buffer before every call (outside its events) so weights come "
-                         "from HBM, and report the median per-call time")
+    ap.add_argument("--no-flush", dest="flush", action="store_false",
+                    help="skip the 1 GiB read before every call (by default it runs, outside the call's "
+                         "events, so that weights come from HBM); the step time is then the wall clock "
+                         "over K back-to-back calls")
     ap.add_argument("--fp8", action="store_true",
                     help="run moe_layer_fp8: expert weights quantised once (moe_quantize_fp8, OCP E4M3 "
                          "with per-channel scales) before timing; activations and h stay bf16; no CPU "
