@@ -1,4 +1,5 @@
-// Grouped SwiGLU expert GEMMs on bf16 MFMA (gfx950, 16x16x32, fp32 accumulate).
+// Grouped SwiGLU expert GEMMs on bf16 MFMA (gfx950, fp32 accumulate): 16x16x32
+// in the streaming kernels, 32x32x16 in the tile kernel.
 //
 // FinDEP review, section 核心公式: one expert costs three GEMMs of m_e x M x H
 // (gate, up, down), and the per-expert batch m_e decides whether they are
@@ -334,6 +335,11 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
 // ring of 32-wide stages all measured equal or slower.)
 
 constexpr int kTBK = 64;                        // k per stage: 128-byte row segments
+// A buffer offset past every token matrix that takes 32-bit offsets (those
+// are below kA32Limit bytes, and a stage adds at most 128 KB): loads from it
+// return zeros without a memory access.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr unsigned long long kA32Limit = 0x7FFF0000ull;
 constexpr int kTN = 256;                        // weight rows per tile
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -378,9 +384,10 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // (four 16-byte pieces, piece c of row r at c ^ ((r >> 2) & 3)); each lane
 // reads its eight codes of a B fragment and widens them to bf16 exactly, and
 // the per-channel scales multiply the sums in the epilogue.
-// A32: the token matrix of every segment spans less than 4 GiB, so token
-// rows are addressed by 32-bit offsets through a buffer resource; otherwise
-// by 64-bit pointers (more registers, used with 128-row tiles only).
+// A32: the token matrix of every segment spans less than kA32Limit bytes
+// (just under 2 GiB), so token rows are addressed by 32-bit offsets through a
+// buffer resource, and padding rows by an offset past it; otherwise by 64-bit
+// pointers (more registers, used with 128-row tiles only).
 template <bool GATEUP, int BM, bool F8, bool A32>
 __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
@@ -499,7 +506,9 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       const int ch = lslot ^ tsw(r);
       const int rr = (r < nrows) ? r : 0;
       const int grow = pa.a_rows ? pa.a_rows[row0 + rr] : (row0 + rr);
-      if constexpr (A32) aoffg[i] = (uint32_t)grow * (uint32_t)(2 * K) + (uint32_t)(ch * 16);
+      // padding rows (past the group's count) take an offset beyond the
+      // buffer: the load writes zeros and reads no memory
+      if constexpr (A32) aoffg[i] = r < nrows ? (uint32_t)grow * (uint32_t)(2 * K) + (uint32_t)(ch * 16) : kOutOfRange;
       else asrc[i] = pa.a + (size_t)grow * K + ch * 8;
     }
 #pragma unroll
@@ -536,9 +545,15 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                   \
       dma16(wrsrc, boffg[i], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * i * (WRB / 2));
 
-    f32x16_t acc[FMW][2];
+    // NBLK: this wave's 32-row blocks that hold rows of the group; the
+    // others (in the group's last row tile only) are padding, whose
+    // multiplications and stores are skipped.  Every wave still issues its
+    // loads and meets every barrier.
+    auto tile_body = [&](auto nblk_c) __attribute__((always_inline)) {
+    constexpr int NBLK = decltype(nblk_c)::value;
+    f32x16_t acc[NBLK > 0 ? NBLK : 1][2];
 #pragma unroll
-    for (int i = 0; i < FMW; ++i)
+    for (int i = 0; i < NBLK; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -582,8 +597,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     }                                                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                             \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                                \
-      u32x4_t af[FMW], bf[2];                                                                      \
-      _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
+      u32x4_t af[NBLK > 0 ? NBLK : 1], bf[2];                                                     \
+      _Pragma("unroll") for (int i = 0; i < NBLK; ++i)                                             \
           af[i] = *reinterpret_cast<const u32x4_t*>((ABUF) + aoff0[s] + 32 * i * kTBK);           \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                              \
         if constexpr (F8) {                                                                        \
@@ -593,7 +608,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
           bf[j] = *reinterpret_cast<const u32x4_t*>((BBUF) + boff0[s] + brow0[j] * kTBK);         \
         }                                                                                          \
       }                                                                                            \
-      _Pragma("unroll") for (int i = 0; i < FMW; ++i)                                              \
+      _Pragma("unroll") for (int i = 0; i < NBLK; ++i)                                             \
           _Pragma("unroll") for (int j = 0; j < 2; ++j)                                            \
               acc[i][j] = mfma32(bf[j], af[i], acc[i][j]);                                          \
     }                                                                                              \
@@ -603,10 +618,10 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     // the loop names each buffer explicitly (see above): stage kt reads token
     // buffer kt % 2 and weight buffer kt % NB, a pattern of period 2 or 6;
     // the remainder continues it step by step
-    int kt = 0;
 #define MOE_A(I) ((I) % NA == 0 ? sa0 : (I) % NA == 1 ? sa1 : sa2)
 #define MOE_B(I) ((I) % NB == 0 ? sb0 : (I) % NB == 1 ? sb1 : sb2)
 #define MOE_USTEP(U, KT_) MOE_TSTEP(MOE_A(U), MOE_A((U) + NA - 1), MOE_B(U), MOE_B((U) + NB - 1), KT_)
+    int kt = 0;
     if constexpr (NA == 2 && NB == 2) {
       for (; kt + 1 < KT; kt += 2) {
         MOE_USTEP(0, kt)
@@ -659,6 +674,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       const int ch = lane & 7;
 #pragma unroll
       for (int i = 0; i < FMW; ++i) {
+        if (i >= NBLK) break;                  // padding rows only
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -682,7 +698,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
         }
         __builtin_amdgcn_wave_barrier();
       }
-      continue;
+      return;
     }
 
     // Gate+up.  acc[i][0] and acc[i][1] hold the gate and up sums of the same
@@ -703,7 +719,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
         }
         const float gs[4] = {sg.x, sg.y, sg.z, sg.w}, us[4] = {su.x, su.y, su.z, su.w};
 #pragma unroll
-        for (int i = 0; i < FMW; ++i) {
+        for (int i = 0; i < NBLK; ++i) {
           const int row = wm * (BM / 2) + 32 * i + fr;
           if (row >= nrows) continue;
           float v[4];
@@ -716,6 +732,21 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       }
+    }
+    };
+    // one instance of the contraction and epilogue per count of live blocks,
+    // so that no accumulator is merged across them
+    const int live = nrows - wm * (BM / 2);
+    const int nblk = live <= 0 ? 0 : min(FMW, ceil_div(live, 32));
+    if (nblk == FMW) {
+      tile_body(std::integral_constant<int, FMW>{});
+    } else if (nblk == 0) {
+      tile_body(std::integral_constant<int, 0>{});
+    } else if (nblk == 1) {
+      tile_body(std::integral_constant<int, 1>{});
+    } else if constexpr (FMW >= 3) {
+      if (nblk == 2) tile_body(std::integral_constant<int, 2>{});
+      else if constexpr (FMW >= 4) tile_body(std::integral_constant<int, 3>{});
     }
   }
 }
@@ -802,7 +833,7 @@ template <bool GATEUP, bool F8>
 hipError_t launch_tile(const FfnArgs& a_in, const FfnArgs& a2_in, int num_cu, hipStream_t st) {
   FfnArgs a = a_in, a2 = a2_in;
   const unsigned long long tb = token_bytes(a), tb2 = a2.E > 0 ? token_bytes(a2) : 0;
-  if (tb > 0xFFFFFFFFull || tb2 > 0xFFFFFFFFull) return launch_tile_bm<GATEUP, 128, F8, false>(a, a2, num_cu, st);
+  if (tb > kA32Limit || tb2 > kA32Limit) return launch_tile_bm<GATEUP, 128, F8, false>(a, a2, num_cu, st);
   a.a_bytes = (uint32_t)tb;
   a2.a_bytes = (uint32_t)tb2;
   const double mean = (double)a.rows_total / (a.E > 0 ? a.E : 1);
