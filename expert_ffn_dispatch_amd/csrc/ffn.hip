@@ -352,6 +352,72 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
 // 8 chunks of 16 B per row: chunk c of row r lives at slot c ^ g(r)
 __device__ __forceinline__ int tsw(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
 
+// Swizzle of the down epilogue's 32 x 64 staging block (row r, 16-byte chunk
+// c, 8-byte half h at chunk c ^ stg_chunk(r), half h ^ stg_half(r)).  A
+// ds_write_b64 of 32 lanes (rows 0..31, one chunk and half) covers 256 bytes:
+// with 64 four-byte banks a row's 128 bytes take the bank half given by r & 1,
+// and (r & 1, chunk, half) must be distinct for all 32 rows, which this
+// mapping makes a bijection of r; with 32 banks, 16 lanes (rows 0..15) must be
+// distinct in (chunk, half), which it also is.  Plain c ^ (r & 7) left rows r,
+// r+8, r+16, r+24 on one bank pair.
+__device__ __forceinline__ int stg_chunk(int r) { return (r & 7) ^ ((r >> 4) & 1); }
+__device__ __forceinline__ int stg_half(int r) { return (r >> 3) & 1; }
+
+// The routed groups' tile list, held in registers so that the stage buffers
+// can take the whole LDS: lane l of every wave owns groups 4l .. 4l+3 (at most
+// 256 groups), with their row offsets and the inclusive prefix of their tile
+// counts; a tile's group is found with one ballot and a few lane reads.
+struct RegTiles {
+  int off[5];     // offsets of groups 4l .. 4l+4
+  int tp[4];      // tiles of groups 0 .. 4l+i, inclusive
+  int total;
+};
+
+template <int BM>
+__device__ __forceinline__ RegTiles reg_tile_list(const FfnArgs& p, int col_tiles, int lane) {
+  RegTiles r;
+  const int E = p.E;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int e = 4 * lane + i;
+    r.off[i] = e <= E ? (p.fixed_rows > 0 ? (e == 0 ? 0 : p.fixed_rows) : p.offsets[e]) : 0;
+  }
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    if (e < E) sum += ceil_div(r.off[i + 1] - r.off[i], BM) * col_tiles;
+    r.tp[i] = sum;
+  }
+  int inc = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.tp[i] += inc - sum;
+  r.total = __shfl(inc, 63);
+  return r;
+}
+
+// Group of routed tile t (t < total): its index, the first tile of the group,
+// its first row and its row count (wave-uniform results).
+__device__ __forceinline__ void reg_find(const RegTiles& r, int t, int& e, int& first, int& base, int& cnt) {
+  const int L = (int)__builtin_ctzll(__ballot(r.tp[3] > t));
+  int tp[4], off[5];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tp[i] = __builtin_amdgcn_readlane(r.tp[i], L);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) off[i] = __builtin_amdgcn_readlane(r.off[i], L);
+  const int prev = L > 0 ? __builtin_amdgcn_readlane(r.tp[3], L > 0 ? L - 1 : 0) : 0;
+  const int i = (tp[0] <= t) + (tp[1] <= t) + (tp[2] <= t);
+  e = 4 * L + i;
+  first = i == 0 ? prev : i == 1 ? tp[0] : i == 2 ? tp[1] : tp[2];
+  base = i == 0 ? off[0] : i == 1 ? off[1] : i == 2 ? off[2] : off[3];
+  cnt = (i == 0 ? off[1] : i == 1 ? off[2] : i == 2 ? off[3] : off[4]) - base;
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l writes
 // lds + 16 l (the LDS address must be the same in every lane).  A plain
 // function, so that kernel templates call no target builtin directly.
@@ -405,7 +471,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   // Every buffer is an array of its own: the compiler then knows that loads
   // into one buffer do not touch the reads of another (as parts of one array
   // it waits for the loads before every read).
-  constexpr int NB = BM == 256 ? 2 : 3;
+  constexpr int NB = (BM == 256 && F8) ? 2 : 3;
   // (three token buffers, with two or three weight buffers: 5% slower with
   // bf16 weights, within 1% with FP8)
   constexpr int NA = 2;
@@ -416,14 +482,13 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   // output through LDS as whole row segments (FP8 Qwen3-235B-shaped layer
   // 3.37 -> 3.19 ms for the swap, 2.92 -> 2.72 ms for the staging; with
   // D[token row][weight row] lanes would hold columns and store 2 bytes).
+  // (256-row bf16 tiles: five 32 KB buffers, the whole 160 KB of LDS)
   __shared__ __align__(16) uint16_t sa0[STA];
   __shared__ __align__(16) uint16_t sa1[STA];
-  __shared__ __align__(16) uint16_t sa2[NA == 3 ? STA : 8];
   __shared__ __align__(16) uint16_t sb0[STB];
   __shared__ __align__(16) uint16_t sb1[STB];
   __shared__ __align__(16) uint16_t sb2[NB == 3 ? STB : 8];
-  __shared__ int s_off[kMaxGroups + 1];
-  __shared__ int s_tp[kMaxGroups + 1];
+  static_assert(NA == 2, "token rows are double-buffered");
 
   // the wave index as a scalar: the weight rows a wave loads come from one
   // matrix, so their base address stays in scalar registers
@@ -436,7 +501,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   const int NT = ceil_div(p.ncols, HC);          // the last column tile may be partial
   const int RT2 = p2.E > 0 ? ceil_div(p2.fixed_rows, BM) : 0;
   const int T2 = RT2 * ceil_div(p2.ncols, HC);
-  const int total = T2 + build_tile_list<BM>(p, NT, s_off, s_tp);
+  const RegTiles tl = reg_tile_list<BM>(p, NT, lane);
+  const int total = T2 + tl.total;
   const int G = gridDim.x;                       // a multiple of 8
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int fr = lane & 31, fg = lane >> 5;
@@ -475,11 +541,10 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       base = 0;
     } else {
       const int t1 = tile - T2;
-      e = find_group(s_tp, p.E, t1);
-      cnt = s_off[e + 1] - s_off[e];
+      int first;
+      reg_find(tl, t1, e, first, base, cnt);
       RT = ceil_div(cnt, BM);
-      local = t1 - s_tp[e];
-      base = s_off[e];
+      local = t1 - first;
     }
     const int ct = local / RT, rt = local - ct * RT;
     const int row0 = base + rt * BM;
@@ -519,20 +584,6 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       if (wc >= ncols) wc = col0;                // partial column tile: any valid row
       boffg[i] = (uint32_t)wc * (uint32_t)(K * WB) + (uint32_t)(ch * 16);
     }
-    // down: the scale and output row of this lane's token rows (one per
-    // 32-row block), loaded now, used by the epilogue after the whole
-    // contraction
-    float rsc[FMW];
-    int orow_i[FMW];
-    if constexpr (!GATEUP) {
-#pragma unroll
-      for (int i = 0; i < FMW; ++i) {
-        const int row = wm * (BM / 2) + 32 * i + fr;
-        const bool in = row < nrows;
-        rsc[i] = (pa.row_scale && in) ? pa.row_scale[row0 + row] : 1.f;
-        orow_i[i] = (pa.out_rows && in) ? pa.out_rows[row0 + row] : row0 + row;
-      }
-    }
     const int ldsA = ((BM / 8) * wave) * kTBK;
     const int ldsB = (32 * wave) * (WRB / 2);
 
@@ -561,92 +612,94 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 
     // the previous tile's last reads of the buffers are done
     __syncthreads();
-    // issue order: weights of stage 0, tokens of stage 0 (three weight
-    // buffers: then the weights of stage 1)
-    if constexpr (NB == 3 && NA == 2) {
-      MOE_DMA_B(sb0, 0)
-      MOE_DMA_A(sa0, 0)
-      MOE_DMA_B(sb1, min(1, KT - 1))
-    } else {
-      MOE_DMA_A(sa0, 0)
-      MOE_DMA_B(sb0, 0)
-      if (NA == 3) { MOE_DMA_A(sa1, min(1, KT - 1)) }
-      if (NB == 3) { MOE_DMA_B(sb1, min(1, KT - 1)) }
-    }
+    // issue order: weights of stage 0, tokens of stage 0, then (three weight
+    // buffers) the weights of stage 1
+    MOE_DMA_B(sb0, 0)
+    MOE_DMA_A(sa0, 0)
+    if constexpr (NB == 3) { MOE_DMA_B(sb1, min(1, KT - 1)) }
 
-    // One stage: wait for this wave's loads of stage KT_ (with three weight
-    // buffers the weights of stage KT_+1, issued last, may stay in flight),
-    // publish them with the barrier, start the tokens of stage KT_+1 and the
-    // weights of stage KT_+NB-1 into buffers every wave finished reading
-    // before the barrier, multiply stage KT_.  Past the last stage the loads
-    // repeat it (into buffers nobody reads): every step then issues the same
-    // loads, without branches, whose merging costs the compiler its
-    // knowledge of which buffer a load writes.  The scheduling barrier keeps
-    // the loads ahead of the multiplications (left to itself the compiler
-    // sinks them to the end of the step, where they overlap nothing).
-#define MOE_TSTEP(ABUF, NABUF, BBUF, NBBUF, KT_)                                                   \
+    // Fragments of one 16-wide step of a stage (FA: this wave's live token
+    // blocks, FB: its two weight blocks), and the multiplications of a step.
+#define MOE_FRAG(FA, FB, ABUF, BBUF, S_)                                                           \
   {                                                                                                \
-    MOE_WAIT_VM((NA == 3 ? AI : 0) + (NB == 3 ? BI : 0));                                         \
-    __builtin_amdgcn_s_barrier();                                                                  \
-    if constexpr (NA == 3 && NB == 2) {                                                            \
-      MOE_DMA_B(NBBUF, min((KT_) + 1, KT - 1))                                                     \
-      MOE_DMA_A(NABUF, min((KT_) + 2, KT - 1))                                                     \
-    } else {                                                                                       \
-      MOE_DMA_A(NABUF, min((KT_) + NA - 1, KT - 1))                                                \
-      MOE_DMA_B(NBBUF, min((KT_) + NB - 1, KT - 1))                                                \
-    }                                                                                              \
-    __builtin_amdgcn_sched_barrier(0);                                                             \
-    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                                \
-      u32x4_t af[NBLK > 0 ? NBLK : 1], bf[2];                                                     \
-      _Pragma("unroll") for (int i = 0; i < NBLK; ++i)                                             \
-          af[i] = *reinterpret_cast<const u32x4_t*>((ABUF) + aoff0[s] + 32 * i * kTBK);           \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                              \
-        if constexpr (F8) {                                                                        \
-          const uint2 raw_ = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(BBUF) + boff0[s] + brow0[j] * WRB); \
-          bf[j] = e4m3x8_to_bf16x8(raw_.x, raw_.y);                                                \
-        } else {                                                                                   \
-          bf[j] = *reinterpret_cast<const u32x4_t*>((BBUF) + boff0[s] + brow0[j] * kTBK);         \
-        }                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < NBLK; ++i)                                               \
+        FA[i] = *reinterpret_cast<const u32x4_t*>((ABUF) + aoff0[S_] + 32 * i * kTBK);            \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                \
+      if constexpr (F8) {                                                                          \
+        const uint2 raw_ = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(BBUF) + boff0[S_] + brow0[j] * WRB); \
+        FB[j] = e4m3x8_to_bf16x8(raw_.x, raw_.y);                                                  \
+      } else {                                                                                     \
+        FB[j] = *reinterpret_cast<const u32x4_t*>((BBUF) + boff0[S_] + brow0[j] * kTBK);          \
       }                                                                                            \
-      _Pragma("unroll") for (int i = 0; i < NBLK; ++i)                                             \
-          _Pragma("unroll") for (int j = 0; j < 2; ++j)                                            \
-              acc[i][j] = mfma32(bf[j], af[i], acc[i][j]);                                          \
     }                                                                                              \
+  }
+#define MOE_MMA(FA, FB)                                                                            \
+  _Pragma("unroll") for (int i = 0; i < NBLK; ++i)                                                 \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(FB[j], FA[i], acc[i][j]);
+
+    // One stage: wait for this wave's reads of the previous stage and its
+    // loads of stage KT_ (with three weight buffers the weights of stage
+    // KT_+1, issued last, may stay in flight), publish the loads with the
+    // barrier, start the tokens of stage KT_+1 and the weights of stage
+    // KT_+NB-1 into buffers every wave finished reading before the barrier,
+    // then the four 16-wide steps of stage KT_.  The steps are pipelined by
+    // one across the barrier: the fragments of the last step of a stage are
+    // read before the next stage's barrier and multiplied after it, while the
+    // fragments of the next stage's first step load, so each wave has
+    // multiplications to issue while it waits for its reads.  Past the last
+    // stage the loads repeat it (into buffers nobody reads): every step then
+    // issues the same loads, without branches, whose merging costs the
+    // compiler its knowledge of which buffer a load writes.  The scheduling
+    // barrier keeps the loads ahead of the multiplications (left to itself
+    // the compiler sinks them to the end of the step, where they overlap
+    // nothing).
+#define MOE_PSTEP(ABUF, NABUF, BBUF, NBBUF, KT_, FIRST)                                            \
+  {                                                                                                \
     MOE_WAIT_LGKM0();                                                                              \
+    MOE_WAIT_VM(NB == 3 ? BI : 0);                                                                 \
+    __builtin_amdgcn_s_barrier();                                                                  \
+    MOE_DMA_A(NABUF, min((KT_) + 1, KT - 1))                                                       \
+    MOE_DMA_B(NBBUF, min((KT_) + NB - 1, KT - 1))                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                             \
+    MOE_FRAG(ga, gb, ABUF, BBUF, 0)                                                                \
+    if constexpr (!(FIRST)) { MOE_MMA(fa, fb) }                                                   \
+    MOE_FRAG(fa, fb, ABUF, BBUF, 1)                                                                \
+    MOE_MMA(ga, gb)                                                                                \
+    MOE_FRAG(ga, gb, ABUF, BBUF, 2)                                                                \
+    MOE_MMA(fa, fb)                                                                                \
+    MOE_FRAG(fa, fb, ABUF, BBUF, 3)                                                                \
+    MOE_MMA(ga, gb)                                                                                \
   }
 
     // the loop names each buffer explicitly (see above): stage kt reads token
     // buffer kt % 2 and weight buffer kt % NB, a pattern of period 2 or 6;
     // the remainder continues it step by step
-#define MOE_A(I) ((I) % NA == 0 ? sa0 : (I) % NA == 1 ? sa1 : sa2)
+#define MOE_A(I) ((I) % 2 == 0 ? sa0 : sa1)
 #define MOE_B(I) ((I) % NB == 0 ? sb0 : (I) % NB == 1 ? sb1 : sb2)
-#define MOE_USTEP(U, KT_) MOE_TSTEP(MOE_A(U), MOE_A((U) + NA - 1), MOE_B(U), MOE_B((U) + NB - 1), KT_)
-    int kt = 0;
-    if constexpr (NA == 2 && NB == 2) {
-      for (; kt + 1 < KT; kt += 2) {
-        MOE_USTEP(0, kt)
-        MOE_USTEP(1, kt + 1)
-      }
-      if (kt < KT) MOE_USTEP(0, kt)
-    } else {
-      for (; kt + 5 < KT; kt += 6) {
-        MOE_USTEP(0, kt)
-        MOE_USTEP(1, kt + 1)
-        MOE_USTEP(2, kt + 2)
-        MOE_USTEP(3, kt + 3)
-        MOE_USTEP(4, kt + 4)
-        MOE_USTEP(5, kt + 5)
-      }
-      if (kt < KT) MOE_USTEP(0, kt)
-      if (kt + 1 < KT) MOE_USTEP(1, kt + 1)
-      if (kt + 2 < KT) MOE_USTEP(2, kt + 2)
-      if (kt + 3 < KT) MOE_USTEP(3, kt + 3)
-      if (kt + 4 < KT) MOE_USTEP(4, kt + 4)
+#define MOE_USTEP(U, KT_, FIRST) MOE_PSTEP(MOE_A(U), MOE_A((U) + 1), MOE_B(U), MOE_B((U) + NB - 1), KT_, FIRST)
+    u32x4_t fa[NBLK > 0 ? NBLK : 1], fb[2], ga[NBLK > 0 ? NBLK : 1], gb[2];
+    MOE_USTEP(0, 0, true)
+    int kt = 1;
+    for (; kt + 5 < KT; kt += 6) {
+      MOE_USTEP(1, kt, false)
+      MOE_USTEP(2, kt + 1, false)
+      MOE_USTEP(3, kt + 2, false)
+      MOE_USTEP(4, kt + 3, false)
+      MOE_USTEP(5, kt + 4, false)
+      MOE_USTEP(6, kt + 5, false)
     }
+    if (kt < KT) MOE_USTEP(1, kt, false)
+    if (kt + 1 < KT) MOE_USTEP(2, kt + 1, false)
+    if (kt + 2 < KT) MOE_USTEP(3, kt + 2, false)
+    if (kt + 3 < KT) MOE_USTEP(4, kt + 3, false)
+    if (kt + 4 < KT) MOE_USTEP(5, kt + 4, false)
+    MOE_MMA(fa, fb)                                // the last stage's last step
 #undef MOE_USTEP
 #undef MOE_A
 #undef MOE_B
-#undef MOE_TSTEP
+#undef MOE_PSTEP
+#undef MOE_FRAG
+#undef MOE_MMA
 #undef MOE_DMA_A
 #undef MOE_DMA_B
     MOE_WAIT_VM(0);
@@ -658,9 +711,22 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       // rows) it reached HBM as about 1.8x its bytes.  Each wave stages one
       // 32 x 64 block at a time in a 4 KB slot of the token buffers, which
       // every wave has finished reading; 16-byte chunk c of row r sits at
-      // c ^ (r & 7), so neither the writes nor the reads conflict.  FP8:
-      // the per-channel scales of this lane's columns, four at a time.
+      // c ^ stg_chunk(r) with its 8-byte halves swapped where stg_half(r), so
+      // neither the 8-byte writes nor the 16-byte reads conflict.  FP8: the
+      // per-channel scales of this lane's columns, four at a time.
       constexpr int RB = BM / 2;
+      // the scale and output row of this lane's token rows (one per live
+      // 32-row block), loaded after the contraction so that they hold no
+      // registers during it
+      float rsc[NBLK > 0 ? NBLK : 1];
+      int orow_i[NBLK > 0 ? NBLK : 1];
+#pragma unroll
+      for (int i = 0; i < NBLK; ++i) {
+        const int row = wm * RB + 32 * i + fr;
+        const bool in = row < nrows;
+        rsc[i] = (pa.row_scale && in) ? pa.row_scale[row0 + row] : 1.f;
+        orow_i[i] = (pa.out_rows && in) ? pa.out_rows[row0 + row] : row0 + row;
+      }
       __syncthreads();
       uint16_t* blk = (wave < 4 ? sa0 : sa1) + (wave & 3) * 32 * 64;
       const int c = col0 + wn * 64;
@@ -683,14 +749,16 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
             const float4 g = sc4[j][b];
             const uint2 v = make_uint2(pack_bf16x2(a0[4 * b] * g.x * rsc[i], a0[4 * b + 1] * g.y * rsc[i]),
                                        pack_bf16x2(a0[4 * b + 2] * g.z * rsc[i], a0[4 * b + 3] * g.w * rsc[i]));
-            *reinterpret_cast<uint2*>(blk + fr * 64 + (((4 * j + b) ^ (fr & 7)) << 3) + 4 * fg) = v;
+            *reinterpret_cast<uint2*>(blk + fr * 64 + (((4 * j + b) ^ stg_chunk(fr)) << 3) +
+                                      4 * (fg ^ stg_half(fr))) = v;
           }
         __builtin_amdgcn_wave_barrier();       // a wave's LDS operations complete in order
         if (c < ncols) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int r = 8 * t + (lane >> 3);
-            const uint4 v = *reinterpret_cast<const uint4*>(blk + r * 64 + ((ch ^ (r & 7)) << 3));
+            uint4 v = *reinterpret_cast<const uint4*>(blk + r * 64 + ((ch ^ stg_chunk(r)) << 3));
+            if (stg_half(r)) v = make_uint4(v.z, v.w, v.x, v.y);    // (t & 1: known at compile time)
             const int orow = __shfl(orow_i[i], r);
             if (wm * RB + 32 * i + r < nrows)
               *reinterpret_cast<uint4*>(pa.out + (size_t)orow * ncols + c + ch * 8) = v;

@@ -1,6 +1,6 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
 
-    python -m expert_ffn_dispatch_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
+    python -m expert_ffn_dispatch_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>" [<kernel_trace.csv>]
     python -m expert_ffn_dispatch_amd.profiling traffic <fetch counter_collection.csv>
         <write counter_collection.csv> <kernel substring> <copy bytes> <out.txt> "<command>"
     python -m expert_ffn_dispatch_amd.profiling counters <out.md> "<command>" "<note>"
@@ -34,12 +34,30 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def summarize_stats(stats_csv: str, out_md: str, command: str) -> str:
+def _trace_durations(trace_csv: str):
+    """kernel name -> list of dispatch durations (ns), in dispatch order."""
+    out = {}
+    if not trace_csv or not os.path.exists(trace_csv):
+        return out
+    for r in csv.DictReader(open(trace_csv)):
+        out.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
+def summarize_stats(stats_csv: str, out_md: str, command: str, trace_csv: str = "") -> str:
+    """Per-kernel table from the --stats summary; with the kernel trace also
+    the median dispatch and the mean without the first dispatch (the first
+    call of a kernel runs on cold caches and clocks)."""
     rows = list(csv.DictReader(open(stats_csv)))
+    dur = _trace_durations(trace_csv)
     lines = [f"# rocprofv3 kernel statistics", "", f"command: `{command}`", "",
-             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg us | median us | avg w/o first us | min us | max us | share % |",
+             "|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        d = dur.get(r["Name"], [])
+        med = f"{statistics.median(d) / 1e3:.1f}" if d else "-"
+        rest = f"{statistics.mean(d[1:]) / 1e3:.1f}" if len(d) > 1 else "-"
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {med} | {rest} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
     text = "\n".join(lines) + "\n"
     with open(out_md, "w") as f:
@@ -135,7 +153,8 @@ def read_traffic(path: str):
 
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
-        print(summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4]))
+        # stats <kernel_stats.csv> <out.md> "<command>" [<kernel_trace.csv>]
+        print(summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5] if len(sys.argv) > 5 else ""))
     elif sys.argv[1] == "traffic":
         print(summarize_traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7]))
     elif sys.argv[1] == "counters":
