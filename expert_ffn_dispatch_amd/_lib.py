@@ -21,7 +21,10 @@ EXPORTS = (
     "moe_grouped_ffn_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
     "moe_layer", "moe_set_stage_events", "moe_quantize_fp8", "moe_grouped_ffn_fp8", "moe_layer_fp8",
     "moe_layer_pipelined_workspace_bytes", "moe_layer_pipelined", "moe_layer_single_launch",
+    "moe_layer_noalloc",
 )
+# bytes of the library's own workspace array (moe_layer_noalloc)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_STAGE_EVENTS = 7
 
 
@@ -74,6 +77,7 @@ def load() -> ctypes.CDLL:
                                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_layer_pipelined.argtypes = [DIMS, ctypes.c_uint32, ctypes.c_int32] + [P] * 13 + [ctypes.c_size_t, P]
     lib.moe_layer_single_launch.argtypes = [DIMS, ctypes.c_uint32, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.moe_layer_noalloc.argtypes = [DIMS, ctypes.c_uint32] + [P] * 12 + [P]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib

@@ -153,6 +153,24 @@ def moe_layer(d: MoeDims, x, w_gate, w_up, w_down, w_router=None, router_bias=No
     return out
 
 
+def moe_layer_noalloc(d: MoeDims, x, w_gate, w_up, w_down, w_router=None, router_bias=None, ws_gate=None,
+                      ws_up=None, ws_down=None, topk_ids=None, topk_weights=None, ids_in: bool = False, out=None,
+                      stream=None):
+    """moe_layer with the library's own workspace array: nothing is
+    allocated for the call except `out` when the caller passes none."""
+    dev = x.device
+    flags = MOE_FLAG_IDS_IN if ids_in else 0
+    if out is None:
+        out = torch.empty((d.n_tokens, d.hidden), dtype=torch.bfloat16, device=dev)
+    _lib.check(_lib.load().moe_layer_noalloc(
+        ctypes.byref(d), flags, _ptr(x, _BF16_LIKE), _ptr(w_router, _BF16_LIKE),
+        _ptr(router_bias, (torch.float32,)), _ptr(w_gate, _BF16_LIKE), _ptr(w_up, _BF16_LIKE),
+        _ptr(w_down, _BF16_LIKE), _ptr(ws_gate, _BF16_LIKE), _ptr(ws_up, _BF16_LIKE),
+        _ptr(ws_down, _BF16_LIKE), _ptr(topk_ids, (torch.int32,)), _ptr(topk_weights, (torch.float32,)),
+        _ptr(out, _BF16_LIKE), _stream(stream)))
+    return out
+
+
 class Fp8Weights:
     """FP8 (OCP E4M3) expert weights with one float32 scale per output channel:
     codes `gate`/`up` [E][H][M] and `down` [E][M][H] (torch.uint8), scales

@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_ffn.h"
@@ -587,6 +588,30 @@ int run_layer_pipelined(const char* fn, const moe_dims* dims, uint32_t flags, in
   return ok();
 }
 
+// Workspace of moe_layer_noalloc: one array per GPU, in the code object's
+// device memory.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, once per
+// device (with that device current), and only that address is used.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+int scratch_address(const char* fn, void** ptr) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return device_error(fn, e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return device_error(fn, e);
+    if (p == nullptr) return fail(MOE_ERR_DEVICE, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -794,6 +819,36 @@ int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe
   }
   return run_layer(fn, dims, flags, x, w_router, router_bias, bf16_weights(w_gate, w_up, w_down),
                    bf16_weights(ws_gate, ws_up, ws_down), topk_ids, topk_weights, out, ws, ws_bytes, stream);
+}
+
+int moe_layer_noalloc(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,
+                      const float* router_bias, const moe_bf16* w_gate, const moe_bf16* w_up,
+                      const moe_bf16* w_down, const moe_bf16* ws_gate, const moe_bf16* ws_up,
+                      const moe_bf16* ws_down, int32_t* topk_ids, float* topk_weights, moe_bf16* out,
+                      moe_stream stream) {
+  const char* fn = "moe_layer_noalloc";
+  if (int r = check_dims(fn, dims, true)) return r;
+  REQ_PTR(w_gate);
+  REQ_PTR(w_up);
+  REQ_PTR(w_down);
+  if (dims->n_shared > 0) {
+    REQ_PTR(ws_gate);
+    REQ_PTR(ws_up);
+    REQ_PTR(ws_down);
+  } else if (ws_gate || ws_up || ws_down) {
+    return fail(MOE_ERR_INVALID, "%s: shared-expert weights given with n_shared = 0", fn);
+  }
+  if (int r = check_layer_args(fn, flags, x, w_router, router_bias, topk_ids, topk_weights, out)) return r;
+  Carver sz(nullptr);
+  carve_layer(sz, *dims);
+  if (sz.off > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "%s: this shape needs %zu bytes of workspace, above the %zu of the library's "
+                "scratch array (use moe_layer with a workspace)", fn, sz.off, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  if (int r = scratch_address(fn, &ptr)) return r;
+  return run_layer(fn, dims, flags, x, w_router, router_bias, bf16_weights(w_gate, w_up, w_down),
+                   bf16_weights(ws_gate, ws_up, ws_down), topk_ids, topk_weights, out, ptr,
+                   MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moe_layer_fp8(const moe_dims* dims, uint32_t flags, const moe_bf16* x, const moe_bf16* w_router,

@@ -279,6 +279,30 @@ int moe_layer(const moe_dims* dims, uint32_t flags, const moe_bf16* x,
               void* ws, size_t ws_bytes, moe_stream stream);
 
 /*
+ * moe_layer_noalloc - moe_layer without a workspace argument, for callers that
+ * cannot allocate device memory: code recorded under HIP graph capture, tight
+ * serving loops, and harnesses that forbid hipMalloc.  The workspace is an
+ * array inside the library, MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it
+ * runs on, held until the process ends; its address is looked up once per
+ * device, on the first call with that device current.  The call allocates
+ * nothing (no hipMalloc, no hipFree).
+ *
+ * Arguments and results as for moe_layer.  Shapes whose
+ * moe_layer_workspace_bytes exceed MOE_NOALLOC_SCRATCH_BYTES are rejected
+ * with MOE_ERR_WORKSPACE before anything is enqueued (decode-sized batches
+ * fit: e.g. N = 512 tokens of M = 2048, E = 128, k = 8, H = 768 need 29 MiB).
+ * Every call on one GPU shares that GPU's array and nothing in it has to
+ * start at zero, but calls that overlap on one GPU (two streams, two
+ * threads) race on it: the caller must order them.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_noalloc(const moe_dims* dims, uint32_t flags, const moe_bf16* x,
+                      const moe_bf16* w_router, const float* router_bias,
+                      const moe_bf16* w_gate, const moe_bf16* w_up, const moe_bf16* w_down,
+                      const moe_bf16* ws_gate, const moe_bf16* ws_up, const moe_bf16* ws_down,
+                      int32_t* topk_ids, float* topk_weights, moe_bf16* out, moe_stream stream);
+
+/*
  * moe_layer_fp8 - moe_layer with FP8 weights for the routed experts and, if
  * n_shared > 0, the shared experts (their concatenation [S*Hs][M] and
  * [M][S*Hs] quantised as one matrix each, one scale per output channel).

@@ -114,6 +114,27 @@ def test_layer_argument_rules(lib):
     assert _layer(lib, d, ws=FAKE + 16, ws_bytes=1 << 30) == _lib.MOE_ERR_WORKSPACE
 
 
+def test_noalloc_argument_rules(lib):
+    """moe_layer_noalloc: the moe_layer rules, and shapes whose workspace
+    exceeds the library's array are refused before any device call."""
+    def call(d, flags=0, **over):
+        a = dict(x=FAKE, w_router=FAKE, router_bias=None, w_gate=FAKE, w_up=FAKE, w_down=FAKE, ws_gate=None,
+                 ws_up=None, ws_down=None, topk_ids=None, topk_weights=None, out=FAKE)
+        a.update(over)
+        return lib.moe_layer_noalloc(ctypes.byref(d), flags, a["x"], a["w_router"], a["router_bias"], a["w_gate"],
+                                     a["w_up"], a["w_down"], a["ws_gate"], a["ws_up"], a["ws_down"], a["topk_ids"],
+                                     a["topk_weights"], a["out"], None)
+    assert call(D(N=0)) == _lib.MOE_ERR_INVALID and "n_tokens" in _err(lib)
+    assert call(D(), flags=8) == _lib.MOE_ERR_INVALID and "flags" in _err(lib)
+    assert call(D(), w_gate=None) == _lib.MOE_ERR_INVALID and "w_gate" in _err(lib)
+    assert call(D(), x=MIS) == _lib.MOE_ERR_INVALID and "aligned" in _err(lib)
+    big = D(N=8192, M=4096, E=128, k=8, H=1536)
+    assert moe.moe_layer_workspace_bytes(big, 0) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(big) == _lib.MOE_ERR_WORKSPACE and "scratch" in _err(lib)
+    fits = D(N=512, M=2048, E=128, k=8, H=768)
+    assert moe.moe_layer_workspace_bytes(fits, 0) <= _lib.MOE_NOALLOC_SCRATCH_BYTES
+
+
 def test_other_entry_points_reject(lib):
     d = D()
     assert lib.moe_permute(ctypes.byref(d), None, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
