@@ -117,6 +117,7 @@ struct LayerWs {
   int32_t* a2s;
   int32_t* row_token;
   float* row_weight;
+  int32_t* queue;        // tile queues of the routed and shared gate+up and down launches (zeroed by the permutation)
   PermuteWs perm;
   uint16_t* h;
   uint16_t* y;
@@ -150,6 +151,7 @@ LayerWs carve_layer(Carver& c, const moe_dims& d) {
   w.a2s = c.take<int32_t>(A);
   w.row_token = c.take<int32_t>(A);
   w.row_weight = c.take<float>(A);
+  w.queue = c.take<int32_t>(4 * moe::kQueueWords);
   w.perm = carve_permute(c, (int)A, (int)E);
   w.h = c.take<uint16_t>(A * d.expert_width);
   w.y = c.take<uint16_t>(A * d.hidden);
@@ -281,8 +283,11 @@ int run_grouped_ffn(const char* fn, const moe_dims* dims, const moe_bf16* x_sort
   const int ncu = num_cus();
   if (ncu <= 0) return fail(MOE_ERR_DEVICE, "%s: cannot query the device", fn);
   const int A = dims->n_tokens * dims->top_k;
-  uint16_t* h = static_cast<uint16_t*>(ws);
+  Carver c(ws);
+  uint16_t* h = c.take<uint16_t>((size_t)A * dims->expert_width);
+  int32_t* queue = c.take<int32_t>(2 * moe::kQueueWords);
   moe::FfnArgs g = gateup_args(wt);
+  g.queue = queue;
   g.a = x_sorted;
   g.offsets = expert_offsets;
   g.out = h;
@@ -292,6 +297,7 @@ int run_grouped_ffn(const char* fn, const moe_dims* dims, const moe_bf16* x_sort
   g.ncols = dims->expert_width;
   if (hipError_t e = moe::launch_ffn_gateup(g, ncu, st)) return device_error(fn, e);
   moe::FfnArgs dn = down_args(wt);
+  dn.queue = queue + moe::kQueueWords;
   dn.a = h;
   dn.offsets = expert_offsets;
   dn.row_scale = row_scale;
@@ -400,7 +406,7 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
   }
   if (hipError_t e = mark(1)) return device_error(fn, e);
   moe::PermuteArgs p{ids, A, E, k, w.counts, w.offsets, w.s2a, w.a2s, w.row_token, wts, w.row_weight,
-                     w.perm.tile_hist, w.perm.tile_off};
+                     w.perm.tile_hist, w.perm.tile_off, w.queue, 4 * moe::kQueueWords};
   if (hipError_t e = moe::launch_permute(p, st)) return device_error(fn, e);
   if (hipError_t e = mark(2)) return device_error(fn, e);
   if (order.before != nullptr) {
@@ -431,6 +437,9 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
     sd.rows_total = N;
     sd.K = SH;
     sd.ncols = M;
+    sg.queue = w.queue + 2 * moe::kQueueWords;
+    sd.queue = w.queue + 3 * moe::kQueueWords;
+    sg.queue_zeroed = sd.queue_zeroed = true;
   }
   if (hipError_t e = mark(3)) return device_error(fn, e);
   moe::FfnArgs g = gateup_args(routed);
@@ -443,6 +452,8 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
   g.rows_total = A;
   g.K = M;
   g.ncols = H;
+  g.queue = w.queue;
+  g.queue_zeroed = true;
   if (hipError_t e = has_shared ? moe::launch_ffn_gateup_shared(g, sg, ncu, st) : moe::launch_ffn_gateup(g, ncu, st))
     return device_error(fn, e);
   if (hipError_t e = mark(4)) return device_error(fn, e);
@@ -460,6 +471,8 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
   dn.K = H;
   dn.ncols = M;
   dn.out_rows = direct ? w.row_token : nullptr;
+  dn.queue = w.queue + moe::kQueueWords;
+  dn.queue_zeroed = true;
   if (hipError_t e = has_shared ? moe::launch_ffn_down_shared(dn, sd, ncu, st) : moe::launch_ffn_down(dn, ncu, st))
     return device_error(fn, e);
   if (order.after != nullptr) {
@@ -683,6 +696,7 @@ int moe_grouped_ffn_workspace_bytes(const moe_dims* dims, size_t* bytes) {
   if (bytes == nullptr) return fail(MOE_ERR_INVALID, "%s: bytes is NULL", fn);
   Carver c(nullptr);
   c.take<uint16_t>((size_t)dims->n_tokens * dims->top_k * dims->expert_width);
+  c.take<int32_t>(2 * moe::kQueueWords);
   *bytes = c.off;
   return ok();
 }

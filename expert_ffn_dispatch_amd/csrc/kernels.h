@@ -32,7 +32,11 @@ struct PermuteArgs {
   float* row_weight;         // [A] weight in sorted order, or null
   int32_t* tile_hist;        // [E][T] workspace
   int32_t* tile_off;         // [E][T] workspace
+  int32_t* zero = nullptr;   // n_zero ints set to zero on the way (the expert GEMMs' tile queues)
+  int n_zero = 0;
 };
+// n ints of device memory set to zero (one small launch)
+hipError_t launch_zero_words(int32_t* p, int n, hipStream_t st);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
 
 // x_sorted[p] = x[row_token[p]] or x[s2a[p] / k]
@@ -71,7 +75,13 @@ struct FfnArgs {
   const uint8_t* q1 = nullptr;
   const float* s0 = nullptr;
   const float* s1 = nullptr;
+  // eight tile counters of the tile kernel's queues (device, kQueueWords
+  // ints), or null for static dealing; queue_zeroed: they are zero when the
+  // launch starts (else the launcher clears them first)
+  int32_t* queue = nullptr;
+  bool queue_zeroed = false;
 };
+constexpr int kQueueWords = 8;
 hipError_t launch_ffn_gateup(const FfnArgs& a, int num_cu, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, int num_cu, hipStream_t st);
 // The routed groups together with the shared experts (shared: E = 1,

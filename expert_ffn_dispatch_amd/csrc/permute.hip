@@ -87,6 +87,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(PermuteArgs p, int T, int 
   __shared__ int wc[4][256];
   __shared__ int s_base[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, tile = blockIdx.x;
+  if (tile == 0 && tid < p.n_zero) p.zero[tid] = 0;
   for (int i = tid; i < 4 * 256; i += 256) (&wc[0][0])[i] = 0;
   // expert offsets: exclusive scan of the counts (every block; block 0 also
   // publishes them)
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(PermuteArgs p, int 
   __shared__ int wc[16][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, A = p.A;
+  if (tid < p.n_zero) p.zero[tid] = 0;
   if (tid < E) {
     cnt[tid] = 0;
     base[tid] = 0;
@@ -253,6 +255,16 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
 }
 
 }  // namespace
+
+__global__ __launch_bounds__(64) void zero_words_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0;
+}
+
+hipError_t launch_zero_words(int32_t* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, st, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   const int T = ceil_div(a.A, kPermTile);
