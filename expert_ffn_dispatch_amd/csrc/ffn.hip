@@ -634,6 +634,9 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 #define MOE_DMA_B(BUF, KT_)                                                                        \
   _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                   \
       dma16(wrsrc, boffg[i], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * i * (WRB / 2));
+#define MOE_DMA_B1(BUF, KT_, I_)                                                                   \
+  if constexpr ((I_) < BI)                                                                         \
+      dma16(wrsrc, boffg[I_], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * (I_) * (WRB / 2));
 
     // NBLK: this wave's 32-row blocks that hold rows of the group; the
     // others (in the group's last row tile only) are padding, whose
@@ -679,9 +682,15 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     // One stage: wait for this wave's reads of the previous stage and its
     // loads of stage KT_ (with three weight buffers the weights of stage
     // KT_+1, issued last, may stay in flight), publish the loads with the
-    // barrier, start the tokens of stage KT_+1 and the weights of stage
-    // KT_+NB-1 into buffers every wave finished reading before the barrier,
-    // then the four 16-wide steps of stage KT_.  The steps are pipelined by
+    // barrier, start the tokens of stage KT_+1 into a buffer every wave
+    // finished reading before the barrier, then the four 16-wide steps of
+    // stage KT_, each followed by one of the wave's loads of the weights of
+    // stage KT_+NB-1.  (All seven loads at once after the barrier backed up
+    // in the vector L1, whose pending-miss stalls took about half the
+    // kernel's time, and the waves' MFMAs waited behind them; one weight load
+    // per step: Qwen3-235B-shaped gate+up 1575 -> 1498 us, down 930 -> 887,
+    // DeepSeek-V2-shaped gate+up 1209 -> 1170.  Spreading the token loads
+    // too was slower, and the non-temporal hint on these loads much slower.)  The steps are pipelined by
     // one across the barrier: the fragments of the last step of a stage are
     // read before the next stage's barrier and multiplied after it, while the
     // fragments of the next stage's first step load, so each wave has
@@ -696,13 +705,14 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     // the compiler sinks them to the end of the step, where they overlap
     // nothing).
 // Order of one group of a stage: the fragment reads of the next step first,
-// then the multiplications of this one (MMA_: the group has them), and
-// nothing moves across the group's end.
-#define MOE_ORDER(MMA_)                                                                            \
+// then the multiplications of this one (MMA_: the group has them), then its
+// weight load (VM_), and nothing moves across the group's end.
+#define MOE_ORDER(MMA_, VM_)                                                                       \
   if constexpr (NBLK > 0) {                                                                        \
     __builtin_amdgcn_sched_group_barrier(0x100, NBLK + 2, 0);                                      \
     if constexpr (MMA_) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NBLK, 0);                 \
   }                                                                                                \
+  if constexpr (VM_) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                            \
   __builtin_amdgcn_sched_barrier(0);
 #define MOE_PSTEP(ABUF, NABUF, BBUF, NBBUF, KT_, FIRST)                                            \
   {                                                                                                \
@@ -710,20 +720,23 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     MOE_WAIT_VM(NB == 3 ? BI : 0);                                                                 \
     __builtin_amdgcn_s_barrier();                                                                  \
     MOE_DMA_A(NABUF, min((KT_) + 1, KT - 1))                                                       \
-    MOE_DMA_B(NBBUF, min((KT_) + NB - 1, KT - 1))                                                  \
     __builtin_amdgcn_sched_barrier(0);                                                             \
     MOE_FRAG(ga, gb, ABUF, BBUF, 0)                                                                \
     if constexpr (!(FIRST)) { MOE_MMA(fa, fb) }                                                   \
-    MOE_ORDER(!(FIRST))                                                                            \
+    MOE_DMA_B1(NBBUF, min((KT_) + NB - 1, KT - 1), 0)                                              \
+    MOE_ORDER(!(FIRST), BI > 0)                                                                    \
     MOE_FRAG(fa, fb, ABUF, BBUF, 1)                                                                \
     MOE_MMA(ga, gb)                                                                                \
-    MOE_ORDER(true)                                                                                \
+    MOE_DMA_B1(NBBUF, min((KT_) + NB - 1, KT - 1), 1)                                              \
+    MOE_ORDER(true, BI > 1)                                                                        \
     MOE_FRAG(ga, gb, ABUF, BBUF, 2)                                                                \
     MOE_MMA(fa, fb)                                                                                \
-    MOE_ORDER(true)                                                                                \
+    MOE_DMA_B1(NBBUF, min((KT_) + NB - 1, KT - 1), 2)                                              \
+    MOE_ORDER(true, BI > 2)                                                                        \
     MOE_FRAG(fa, fb, ABUF, BBUF, 3)                                                                \
     MOE_MMA(ga, gb)                                                                                \
-    MOE_ORDER(true)                                                                                \
+    MOE_DMA_B1(NBBUF, min((KT_) + NB - 1, KT - 1), 3)                                              \
+    MOE_ORDER(true, BI > 3)                                                                        \
   }
 
     // the loop names each buffer explicitly (see above): stage kt reads token
