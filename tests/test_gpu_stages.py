@@ -83,6 +83,46 @@ def test_route_rows(shape):
     np.testing.assert_allclose(gw[ok], r["topk_weights"][ok], rtol=1e-5, atol=1e-6)
 
 
+# batches of 8192 tokens or more over more than 32 experts: scores and top-k
+# in one launch (32 tokens per block, 4-stage LDS ring over the hidden
+# dimension); ragged last blocks, hidden sizes of 1..5 stages, 48 / 160 / 256
+# padded experts (the three kernel widths)
+FUSED_ROUTE = [
+    (8204, 256, 40, 4, True),     # last block of 12 tokens, 48 padded experts
+    (8192, 320, 160, 6, False),   # five stages: the ring's remainder steps
+    (8192, 128, 256, 8, True),    # two stages (fewer than the ring's depth), most experts
+    (8224, 64, 64, 2, False),     # one stage
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_ROUTE, ids=[str(s) for s in FUSED_ROUTE])
+def test_route_fused(shape):
+    _route_twice(shape)
+
+
+def _route_twice(shape):
+    N, M, E, k, bias = shape
+    note(f"route fused {shape}")
+    d = gen.random_small(N, M, E, k, 128, seed=13, bias=bias, std=0.05)
+    dm = moe.dims(N, M, E, k, 128)
+    t = upload(d)
+    ids, w = moe.moe_route(dm, t["x"], t["w_router"], t.get("router_bias"))
+    ids2, w2 = moe.moe_route(dm, t["x"], t["w_router"], t.get("router_bias"))
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    r = O.route(d["x"], d["w_router"], k, d.get("router_bias"))
+    ok = r["margin"] >= TIE_MARGIN
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    note(f"  near-tie tokens: {(~ok).sum()} of {N}")
+    assert ok.sum() > N // 2
+    assert np.array_equal(gi[ok], r["topk_ids"][ok])
+    np.testing.assert_allclose(gw[ok], r["topk_weights"][ok], rtol=1e-5, atol=1e-6)
+    assert np.abs(gw.astype(np.float64).sum(1) - 1).max() < 1e-5
+    # every token's ids are k distinct experts in range, including near ties
+    assert (gi >= 0).all() and (gi < E).all()
+    assert all(len(set(row)) == k for row in gi.tolist())
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s[:5]) for s in SHAPES])
 def test_permute_bit_exact(shape):
     d, dm = _case(shape)
