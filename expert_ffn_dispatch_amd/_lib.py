@@ -6,7 +6,9 @@ loudly if it is missing: there is no fallback implementation.
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ffn.so")
+# MOE_FFN_LIB names another build of the same library (the host-sanitizer
+# build, libmoe_ffn_san.so) to load instead of the in-tree one.
+LIB_PATH = os.environ.get("MOE_FFN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ffn.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID = 1
