@@ -25,11 +25,12 @@
 //  * tile (large groups): 128/192/256-row x 256-column tiles, both operands
 //    loaded straight into LDS in 64-wide stages (16-byte chunks XOR-swizzled
 //    by row so MFMA fragment reads are free of bank conflicts), eight waves
-//    of (rows/2) x 64.  Tiles are ordered row-tile-fastest and dealt to the
-//    eight XCDs in contiguous runs so that tiles sharing weights or rows share
-//    an L2.
-// Both walk a tile list built in LDS from the device-side group offsets, so
-// the host never reads the counts.  Both also take FP8 (OCP E4M3) weights
+//    of (rows/2) x 64.  Tiles are ordered row-tile-fastest and taken from
+//    eight per-XCD queues of contiguous runs, so that tiles sharing weights
+//    or rows share an L2.
+// Both walk a tile list built on the device from the group offsets (the
+// stream kernel's in LDS, the tile kernel's in registers), so the host never
+// reads the counts.  Both also take FP8 (OCP E4M3) weights
 // with one scale per output channel: the codes are widened to bf16 exactly
 // as MFMA fragments are read from LDS, and the scale multiplies the fp32 sum.
 #include <type_traits>
@@ -311,28 +312,27 @@ __global__ __launch_bounds__(256, 2) void ffn_stream_ks_kernel(FfnArgs p) {
 
 // ============================== tiled kernel ===============================
 //
-// 256 rows x 256 weight rows per tile (gate+up: 128 gate and the same 128 up
-// rows, i.e. 128 h columns; down: 256 output columns), eight waves in a 2 x 4
-// grid, each 128 rows x 64 weight rows, bf16 MFMA 32x32x16 (fp32 accumulate).
-// The k loop walks 64-wide stages (128 contiguous bytes of every row, one L2
-// line) through two LDS stage buffers of 64 KB: stage kt+1 is loaded while
-// stage kt is multiplied.  Stages are loaded straight into LDS (16 bytes per
-// lane, no staging registers).  Each buffer is its own LDS array and the
-// loop is unrolled over the two, so the compiler can tell which buffer a load
-// writes and does not wait for it before reading the other; each wave waits
+// BM rows (128, 192 or 256) x 256 weight rows per tile (gate+up: 128 gate
+// and the same 128 up rows, i.e. 128 h columns; down: 256 output columns),
+// eight waves in a 2 x 4 grid, each BM/2 rows x 64 weight rows, bf16 MFMA
+// 32x32x16 (fp32 accumulate).  The k loop walks 64-wide stages (128
+// contiguous bytes of every row, one L2 line): token rows one stage ahead in
+// two LDS buffers, weight rows two stages ahead in three (two for 256-row FP8
+// tiles).  Stages are loaded straight into LDS (16 bytes per lane, no
+// staging registers).  Each buffer is its own LDS array and the loop is
+// unrolled over their period, so the compiler can tell which buffer a load
+// writes and does not wait for it before reading another; each wave waits
 // for its own loads of a stage before the barrier that publishes the stage to
 // the other waves.  A direct LDS load writes 16 bytes per lane at consecutive
 // addresses, so the row swizzle is applied on the source side: the lane that
 // fills slot p of row r fetches chunk p ^ g(r), g(r) = ((r >> 1) ^ ((r & 1)
 // << 2)) & 7, which makes the 32-row fragment reads conflict-free for 32- and
-// 64-bank LDS.  Tiles are ordered row-tile-fastest and dealt to the eight XCDs
-// in contiguous runs, so tiles sharing weights or token rows share an L2.
+// 64-bank LDS.  Tiles are ordered row-tile-fastest (a group's row tiles
+// balanced to within one 32-row block) and taken from per-XCD queues of
+// contiguous runs, so tiles sharing weights or token rows share an L2.
 //
-// Measured on 16 experts x 2048 rows (M=4096, H=1536): ~1.0 PFLOP/s gate+up,
-// ~0.8 down; the same loop without its loads reaches 1.6 / 1.1 and the loads
-// alone take 75% of the full time, so the operand feed from L2 bounds it.
 // (Four waves of 128 x 128, register-staged 32-wide stages and a four-deep
-// ring of 32-wide stages all measured equal or slower.)
+// ring of 32-wide stages all measured equal or slower than eight waves.)
 
 constexpr int kTBK = 64;                        // k per stage: 128-byte row segments
 // A buffer offset past every token matrix that takes 32-bit offsets (those
@@ -401,6 +401,19 @@ __device__ __forceinline__ RegTiles reg_tile_list(const FfnArgs& p, int col_tile
   return r;
 }
 
+// Row tile rt of a group of cnt rows cut into RT tiles of at most BM rows
+// (RT = ceil(cnt / BM)): the group's 32-row blocks are dealt out evenly, so
+// tiles of one group differ by one block at most and a group's padding is
+// under 32 rows.  off: the tile's first row (a multiple of 32); nrows: its
+// live rows.
+__device__ __forceinline__ void row_tile(int cnt, int RT, int rt, int& off, int& nrows) {
+  const int nb = (cnt + 31) >> 5;
+  const int q = nb / RT, r = nb - q * RT;
+  const int b0 = rt * q + min(rt, r);
+  off = 32 * b0;
+  nrows = min(32 * (q + (rt < r ? 1 : 0)), cnt - off);
+}
+
 // Group of routed tile t (t < total): its index, the first tile of the group,
 // its first row and its row count (wave-uniform results).
 __device__ __forceinline__ void reg_find(const RegTiles& r, int t, int& e, int& first, int& base, int& cnt) {
@@ -454,7 +467,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // (just under 2 GiB), so token rows are addressed by 32-bit offsets through a
 // buffer resource, and padding rows by an offset past it; otherwise by 64-bit
 // pointers (more registers, used with 128-row tiles only).
-template <bool GATEUP, int BM, bool F8, bool A32>
+// PF: down tiles whose stage count divides by six (every segment's) load
+// the next tile's first stages in their own last two (see the stage loop).
+template <bool GATEUP, int BM, bool F8, bool A32, bool PF>
 __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
   constexpr int FMW = BM / 64;                   // 32-row MFMA blocks per wave
@@ -518,20 +533,31 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   // contiguous runs per XCD.
   constexpr bool QCAP = !(BM == 256 && !F8);
   int* s_ticket = nullptr;
+  int* s_next = nullptr;
   if constexpr (QCAP) {
-    __shared__ int s_ticket_lds;
-    s_ticket = &s_ticket_lds;
+    __shared__ int s_ticket_lds[2];
+    s_ticket = &s_ticket_lds[0];
+    s_next = &s_ticket_lds[1];
   }
   constexpr bool dyn = QCAP;           // (a runtime choice of the two costs ~20 registers)
-  auto fetch = [&]() -> int {                    // one thread of the block
+  // A ticket of this XCD's queue (one thread of the block).  Its value is
+  // first needed by claim(), stages later, so the atomic's latency is not
+  // spent at the tile start, where every wave waits at the first barrier.
+  auto take = [&]() -> int { return atomicAdd(&p.queue[blockIdx.x & 7], 1); };
+  // The tile of ticket t of this XCD's queue; past its end, a tile of the
+  // other queues in turn; -1 when every queue is exhausted.
+  auto claim = [&](int t) -> int {
     const int tot = total;
     const int x = blockIdx.x & 7;
-    for (int i = 0; i < 8; ++i) {
+    const int lo = (int)(((long long)tot * x) >> 3), hi = (int)(((long long)tot * (x + 1)) >> 3);
+    if (t < hi - lo) return lo + t;
+#pragma nounroll
+    for (int i = 1; i < 8; ++i) {
       const int y = (x + i) & 7;
-      const int lo = (int)(((long long)tot * y) >> 3), hi = (int)(((long long)tot * (y + 1)) >> 3);
-      if (lo >= hi) continue;
-      const int t = atomicAdd(&p.queue[y], 1);
-      if (t < hi - lo) return lo + t;
+      const int lo2 = (int)(((long long)tot * y) >> 3), hi2 = (int)(((long long)tot * (y + 1)) >> 3);
+      if (lo2 >= hi2) continue;
+      const int u = atomicAdd(&p.queue[y], 1);
+      if (u < hi2 - lo2) return lo2 + u;
     }
     return -1;
   };
@@ -557,18 +583,92 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   const int lrow = lane >> 3, lslot = lane & 7;
   const int qrow = lane >> 2, qslot = lane & 3;
 
+  // Tile t's expert, first token row, live rows, first output column and
+  // the row tiles of its group.
+  auto tile_geom = [&](int t, int& e, int& row0, int& nrows, int& col0, int& RT) {
+    int cnt, local, base;
+    e = 0;
+    if (t < T2) {
+      cnt = p2.fixed_rows;
+      RT = RT2;
+      local = t;
+      base = 0;
+    } else {
+      const int t1 = t - T2;
+      int first;
+      reg_find(tl, t1, e, first, base, cnt);
+      RT = ceil_div(cnt, BM);
+      local = t1 - first;
+    }
+    const int ct = local / RT, rt = local - ct * RT;
+    int off;
+    row_tile(cnt, RT, rt, off, nrows);
+    row0 = base + off;
+    col0 = ct * HC;
+  };
+  // The direct loads of a tile of segment q: buffer resources (the weight
+  // rows of a wave, rows 32 wave .. 32 wave + 31, lie all in the gate or all
+  // in the up half of the tile, so one base per wave) and per-lane offsets,
+  // or token-row pointers where !A32.
+  auto tile_loads = [&](const FfnArgs& q, int e, int row0, int nrows, int col0, __amdgpu_buffer_rsrc_t& ar,
+                        __amdgpu_buffer_rsrc_t& wr, uint32_t (&ao)[AI], const uint16_t* (&as)[A32 ? 1 : AI],
+                        uint32_t (&bo)[BI]) {
+    const int K = q.K, ncols = q.ncols;
+    // weight rows as bytes (bf16: 2 per element, FP8: 1)
+    constexpr int WB = F8 ? 1 : 2;
+    const uint8_t* wexp0 = (F8 ? q.q0 : reinterpret_cast<const uint8_t*>(q.w0)) + (size_t)e * ncols * K * WB;
+    const uint8_t* wexp1 =
+        GATEUP ? (F8 ? q.q1 : reinterpret_cast<const uint8_t*>(q.w1)) + (size_t)e * ncols * K * WB : wexp0;
+    ar = buffer_rsrc(q.a, A32 ? q.a_bytes : 0u);
+    wr = buffer_rsrc((GATEUP && 32 * wave >= HC) ? wexp1 : wexp0, (uint32_t)ncols * (uint32_t)(K * WB));
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int r = (BM / 8) * wave + 8 * i + lrow;
+      const int ch = lslot ^ tsw(r);
+      const int rr = (r < nrows) ? r : 0;
+      const int grow = q.a_rows ? q.a_rows[row0 + rr] : (row0 + rr);
+      // padding rows (past the group's count) take an offset beyond the
+      // buffer: the load writes zeros and reads no memory
+      if constexpr (A32) ao[i] = r < nrows ? (uint32_t)grow * (uint32_t)(2 * K) + (uint32_t)(ch * 16) : kOutOfRange;
+      else as[i] = q.a + (size_t)grow * K + ch * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int r = F8 ? 32 * wave + 16 * i + qrow : 32 * wave + 8 * i + lrow;
+      const int ch = F8 ? qslot ^ ((r >> 2) & 3) : lslot ^ tsw(r);
+      int wc = col0 + ((GATEUP && r >= HC) ? r - HC : r);
+      if (wc >= ncols) wc = col0;                // partial column tile: any valid row
+      bo[i] = (uint32_t)wc * (uint32_t)(K * WB) + (uint32_t)(ch * 16);
+    }
+  };
+
+  // PF: every tile's stage count divides by six (the period of the stage
+  // loop's buffer pattern), and each tile loads the next tile's first stages
+  // in its own last two, into the buffers the next tile starts from, so
+  // that they are in flight during this tile's epilogue (pre: this tile's
+  // first stages were loaded so).  Down, with balanced row tiles:
+  // DeepSeek-V2-shaped 773 -> 721 us, Qwen3-235B-shaped 911 -> 885 us.  (A
+  // runtime choice between the two endings of the stage loop took the down
+  // kernel past its registers, hence a kernel of its own.)
+  static_assert(!PF || (!GATEUP && NB == 3 && A32 && BM < 256 && QCAP), "next-tile loads: down, three weight buffers");
+  constexpr bool PFC = PF;
+  bool pre = false;
+
   int tile = slot < total ? slot : -1;
   if (dyn) {
-    if (tid == 0) *s_ticket = fetch();
+    if (tid == 0) *s_ticket = claim(take());
     __syncthreads();
     tile = __builtin_amdgcn_readfirstlane(*s_ticket);   // the same in every lane
   }
   for (int round = 0; tile >= 0; ++round) {
-    // the next tile: its ticket is taken now (the atomic's latency overlaps
-    // the first stage's loads) and published after this tile
+    // the next tile: its ticket is taken now and claimed later (after this
+    // tile, or in its last stages where they load the next tile's first)
     int next = (round + 1) * G + slot;
     if (next >= total) next = -1;
-    if (dyn && tid == 0) next = fetch();
+    int tk = 0;
+    if (dyn && tid == 0) tk = take();
+    bool claimed = false, pre_next = false;    // set in the last stages (PFC)
+    int nx = -1;
     const bool seg2 = tile < T2;
     const FfnArgs& pa = seg2 ? p2 : p;
     const int K = pa.K, ncols = pa.ncols, KT = K / kTBK;
@@ -586,8 +686,9 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       local = t1 - first;
     }
     const int ct = local / RT, rt = local - ct * RT;
-    const int row0 = base + rt * BM;
-    const int nrows = min(BM, cnt - rt * BM);
+    int roff, nrows;
+    row_tile(cnt, RT, rt, roff, nrows);
+    const int row0 = base + roff;
     const int col0 = ct * HC;
     // weight rows as bytes (bf16: 2 per element, FP8: 1)
     constexpr int WB = F8 ? 1 : 2;
@@ -655,10 +756,12 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     // the previous tile's last reads of the buffers are done
     __syncthreads();
     // issue order: weights of stage 0, tokens of stage 0, then (three weight
-    // buffers) the weights of stage 1
-    MOE_DMA_B(sb0, 0)
-    MOE_DMA_A(sa0, 0)
-    if constexpr (NB == 3) { MOE_DMA_B(sb1, min(1, KT - 1)) }
+    // buffers) the weights of stage 1; none where the previous tile loaded them
+    if (!pre) {
+      MOE_DMA_B(sb0, 0)
+      MOE_DMA_A(sa0, 0)
+      if constexpr (NB == 3) { MOE_DMA_B(sb1, min(1, KT - 1)) }
+    }
 
     // Fragments of one 16-wide step of a stage (FA: this wave's live token
     // blocks, FB: its two weight blocks), and the multiplications of a step.
@@ -714,30 +817,37 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   }                                                                                                \
   if constexpr (VM_) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                            \
   __builtin_amdgcn_sched_barrier(0);
-#define MOE_PSTEP(ABUF, NABUF, BBUF, NBBUF, KT_, FIRST)                                            \
+// DA_ / DB_: the loads of a step (token rows of stage S, weight rows of
+// stage S, load I): this tile's, clamped to its last stage (C), or, for
+// stages past it, the next tile's first (N).
+#define MOE_DMA_AC(BUF, S) MOE_DMA_A(BUF, min((S), KT - 1))
+#define MOE_DMA_B1C(BUF, S, I_) MOE_DMA_B1(BUF, min((S), KT - 1), I_)
+#define MOE_PSTEPX(ABUF, NABUF, BBUF, NBBUF, KT_, FIRST, DA_, DB_)                                 \
   {                                                                                                \
     MOE_WAIT_LGKM0();                                                                              \
     MOE_WAIT_VM(NB == 3 ? BI : 0);                                                                 \
     __builtin_amdgcn_s_barrier();                                                                  \
-    MOE_DMA_A(NABUF, min((KT_) + 1, KT - 1))                                                       \
+    DA_(NABUF, (KT_) + 1)                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                             \
     MOE_FRAG(ga, gb, ABUF, BBUF, 0)                                                                \
     if constexpr (!(FIRST)) { MOE_MMA(fa, fb) }                                                   \
-    MOE_DMA_B1(NBBUF, min((KT_) + NB - 1, KT - 1), 0)                                              \
+    DB_(NBBUF, (KT_) + NB - 1, 0)                                                                  \
     MOE_ORDER(!(FIRST), BI > 0)                                                                    \
     MOE_FRAG(fa, fb, ABUF, BBUF, 1)                                                                \
     MOE_MMA(ga, gb)                                                                                \
-    MOE_DMA_B1(NBBUF, min((KT_) + NB - 1, KT - 1), 1)                                              \
+    DB_(NBBUF, (KT_) + NB - 1, 1)                                                                  \
     MOE_ORDER(true, BI > 1)                                                                        \
     MOE_FRAG(ga, gb, ABUF, BBUF, 2)                                                                \
     MOE_MMA(fa, fb)                                                                                \
-    MOE_DMA_B1(NBBUF, min((KT_) + NB - 1, KT - 1), 2)                                              \
+    DB_(NBBUF, (KT_) + NB - 1, 2)                                                                  \
     MOE_ORDER(true, BI > 2)                                                                        \
     MOE_FRAG(fa, fb, ABUF, BBUF, 3)                                                                \
     MOE_MMA(ga, gb)                                                                                \
-    MOE_DMA_B1(NBBUF, min((KT_) + NB - 1, KT - 1), 3)                                              \
+    DB_(NBBUF, (KT_) + NB - 1, 3)                                                                  \
     MOE_ORDER(true, BI > 3)                                                                        \
   }
+#define MOE_PSTEP(ABUF, NABUF, BBUF, NBBUF, KT_, FIRST) \
+  MOE_PSTEPX(ABUF, NABUF, BBUF, NBBUF, KT_, FIRST, MOE_DMA_AC, MOE_DMA_B1C)
 
     // the loop names each buffer explicitly (see above): stage kt reads token
     // buffer kt % 2 and weight buffer kt % NB, a pattern of period 2 or 6;
@@ -745,6 +855,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 #define MOE_A(I) ((I) % 2 == 0 ? sa0 : sa1)
 #define MOE_B(I) ((I) % NB == 0 ? sb0 : (I) % NB == 1 ? sb1 : sb2)
 #define MOE_USTEP(U, KT_, FIRST) MOE_PSTEP(MOE_A(U), MOE_A((U) + 1), MOE_B(U), MOE_B((U) + NB - 1), KT_, FIRST)
+#define MOE_USTEPX(U, KT_, DA_, DB_) \
+  MOE_PSTEPX(MOE_A(U), MOE_A((U) + 1), MOE_B(U), MOE_B((U) + NB - 1), KT_, false, DA_, DB_)
     u32x4_t fa[NBLK > 0 ? NBLK : 1], fb[2], ga[NBLK > 0 ? NBLK : 1], gb[2];
     MOE_USTEP(0, 0, true)
     int kt = 1;
@@ -756,22 +868,70 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       MOE_USTEP(5, kt + 4, false)
       MOE_USTEP(6, kt + 5, false)
     }
-    if (kt < KT) MOE_USTEP(1, kt, false)
-    if (kt + 1 < KT) MOE_USTEP(2, kt + 1, false)
-    if (kt + 2 < KT) MOE_USTEP(3, kt + 2, false)
-    if (kt + 3 < KT) MOE_USTEP(4, kt + 3, false)
-    if (kt + 4 < KT) MOE_USTEP(5, kt + 4, false)
+    constexpr bool pf = PF;
+    if constexpr (pf) {
+      // The loop ended at stage KT - 5 (phase 1): five stages remain, and
+      // stage KT falls on the buffers of a tile's stage 0.  Claim the next
+      // tile (published by the next stage's barrier), then load its tokens of
+      // stage 0 and weights of stages 0 and 1 where this tile's loads past
+      // its end would go.  Without a next tile those loads repeat this
+      // tile's first stages, into buffers nobody reads.
+      if (tid == 0) *s_next = claim(tk);
+      MOE_USTEP(1, kt, false)
+      MOE_USTEP(2, kt + 1, false)
+      MOE_USTEP(3, kt + 2, false)
+      nx = __builtin_amdgcn_readfirstlane(*s_next);
+      claimed = true;
+      pre_next = nx >= 0;
+      __amdgpu_buffer_rsrc_t arN = arsrc, wrN = wrsrc;
+      uint32_t aoN[AI], boN[BI];
+      const uint16_t* asN[A32 ? 1 : AI];
+#pragma unroll
+      for (int i = 0; i < AI; ++i) aoN[i] = aoffg[i];
+#pragma unroll
+      for (int i = 0; i < BI; ++i) boN[i] = boffg[i];
+      int ktN = KT;
+      if (nx >= 0) {
+        int en, r0n, nrn, c0n, rtn;
+        tile_geom(nx, en, r0n, nrn, c0n, rtn);
+        const FfnArgs& qn = nx < T2 ? p2 : p;
+        tile_loads(qn, en, r0n, nrn, c0n, arN, wrN, aoN, asN, boN);
+        ktN = qn.K / kTBK;
+      }
+#define MOE_DMA_AN(BUF, S)                                                                         \
+  _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                   \
+      dma16(arN, aoN[i], (uint32_t)(min((S) - KT, ktN - 1) * 2 * kTBK), (BUF) + ldsA + 8 * i * kTBK);
+#define MOE_DMA_B1N(BUF, S, I_)                                                                    \
+  if constexpr ((I_) < BI)                                                                         \
+      dma16(wrN, boN[I_], (uint32_t)(min((S) - KT, ktN - 1) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * (I_) * (WRB / 2));
+      MOE_USTEPX(4, kt + 3, MOE_DMA_AC, MOE_DMA_B1N)
+      MOE_USTEPX(5, kt + 4, MOE_DMA_AN, MOE_DMA_B1N)
+#undef MOE_DMA_AN
+#undef MOE_DMA_B1N
+    } else {
+      if (kt < KT) MOE_USTEP(1, kt, false)
+      if (kt + 1 < KT) MOE_USTEP(2, kt + 1, false)
+      if (kt + 2 < KT) MOE_USTEP(3, kt + 2, false)
+      if (kt + 3 < KT) MOE_USTEP(4, kt + 3, false)
+      if (kt + 4 < KT) MOE_USTEP(5, kt + 4, false)
+    }
     MOE_MMA(fa, fb)                                // the last stage's last step
 #undef MOE_USTEP
+#undef MOE_USTEPX
 #undef MOE_A
 #undef MOE_B
 #undef MOE_PSTEP
+#undef MOE_PSTEPX
+#undef MOE_DMA_AC
+#undef MOE_DMA_B1C
 #undef MOE_ORDER
 #undef MOE_FRAG
 #undef MOE_MMA
 #undef MOE_DMA_A
 #undef MOE_DMA_B
-    MOE_WAIT_VM(0);
+    // (after the next tile's loads nothing in flight targets sa1 or sb2,
+    // where down stages its output)
+    if (!pf) MOE_WAIT_VM(0);
 
     if constexpr (!GATEUP) {
       // Down: the output goes through LDS so that the stores write whole
@@ -797,7 +957,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
         orow_i[i] = (pa.out_rows && in) ? pa.out_rows[row0 + row] : row0 + row;
       }
       __syncthreads();
-      uint16_t* blk = (wave < 4 ? sa0 : sa1) + (wave & 3) * 32 * 64;
+      uint16_t* blk = PFC ? (wave < 4 ? sa1 : sb2) + (wave & 3) * 32 * 64
+                          : (wave < 4 ? sa0 : sa1) + (wave & 3) * 32 * 64;
       const int c = col0 + wn * 64;
       float4 sc4[2][4];
 #pragma unroll
@@ -873,14 +1034,16 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     };
     // one instance of the contraction and epilogue per count of live blocks,
     // so that no accumulator is merged across them
-    // Gate+up skips padding only in groups of one row tile: where a group
-    // has several, its cheaper last tile runs ahead of the tiles that share
-    // its weights, and each then fetches them (measured on the
-    // Qwen3-235B-shaped launch: 8.0 GB instead of 5.4 GB of L2 fetch, in the
-    // same time).  Down skips it everywhere (4-5% faster on the Qwen3-235B
-    // shape and the expert-node share, for 2.9 instead of 2.25 GB).
+    // Padding blocks are skipped in every tile.  A group's row tiles differ
+    // by one 32-row block at most (row_tile), so the tiles that share its
+    // weights stay in step; with full tiles and one short last tile, the
+    // short one ran ahead of them, each fetched the weights again, and
+    // gate+up skipped padding in one-tile groups only.  Balanced tiles with
+    // the skip: Qwen3-235B-shaped gate+up 1541 -> 1462 us (padding MFMA work
+    // 1.18x -> about 1.03x of the algorithmic), DeepSeek-V2-shaped down
+    // 751 -> 723 us.
     const int live = nrows - wm * (BM / 2);
-    const int nblk = (GATEUP && RT > 1) ? FMW : live <= 0 ? 0 : min(FMW, ceil_div(live, 32));
+    const int nblk = live <= 0 ? 0 : min(FMW, ceil_div(live, 32));
     if (nblk == FMW) {
       tile_body(std::integral_constant<int, FMW>{});
     } else if (nblk == 0) {
@@ -893,12 +1056,18 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     }
     if (dyn) {
       // every wave read this tile's ticket before the tile's barriers
-      if (tid == 0) *s_ticket = next;
-      __syncthreads();
-      next = *s_ticket;
+      if (claimed) {
+        next = nx;                             // claimed in the last stages
+      } else {
+        if (tid == 0) *s_ticket = claim(tk);
+        __syncthreads();
+        next = *s_ticket;
+      }
     }
     tile = __builtin_amdgcn_readfirstlane(next);
+    pre = pre_next;
   }
+  MOE_WAIT_VM(0);                                // loads past the last tile land before the block ends
 }
 #undef MOE_WAIT_VM
 #undef MOE_WAIT_LGKM0
@@ -963,7 +1132,16 @@ hipError_t launch_tile_bm(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipSt
       if (hipError_t e = launch_zero_words(a.queue, kQueueWords, st)) return e;
     }
   }
-  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8, A32>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
+  // down with every segment's contraction a multiple of six 64-wide stages
+  // (expert widths of 384 m, as 1536): the next-tile loads
+  if constexpr (!GATEUP && A32 && BM < 256) {
+    constexpr int kStages6 = 6 * kTBK;
+    if (a.K % kStages6 == 0 && (a2.E == 0 || a2.K % kStages6 == 0)) {
+      hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8, A32, true>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8, A32, false>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
   return hipGetLastError();
 }
 

@@ -25,6 +25,10 @@ SHAPES = [
     (333, 256, 8, 2, 256, 2, 128, False),   # tile kernel with the shared experts in the same launch, ragged
     (600, 256, 6, 3, 384, 1, 256, True),    # the same with 192-row tiles, 300-row groups
     (1800, 256, 6, 3, 384, 1, 256, True),   # the same with 256-row tiles, 900-row groups
+    # down contraction of six stages (H = 384): each down tile loads the next
+    # tile's first stages; more tiles than blocks, so blocks run several
+    (2304, 4096, 8, 2, 384, 0, 0, False),
+    (2304, 4096, 8, 2, 384, 1, 384, True),  # the shared segment too (contraction 384)
 ]
 
 
