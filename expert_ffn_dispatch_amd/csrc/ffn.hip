@@ -440,6 +440,26 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
 __device__ __forceinline__ void dma16(const uint8_t* g, uint16_t* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
+// A block barrier for the block's LDS reads and writes (not its direct
+// loads into LDS, which the stage barriers publish after each wave's own
+// vmcnt wait): each wave's LDS operations complete (lgkmcnt), then the
+// barrier; the empty asm statements keep the compiler from moving memory
+// accesses across it.  __syncthreads would also wait for every vector-memory
+// operation in flight (its fence covers global memory, and a release fence
+// for LDS alone still waits for the direct loads into LDS), which in the
+// tile kernel are the next tile's first loads and the last tile's stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 4 bytes per lane: lane l writes lds + 4 l.
+__device__ __forceinline__ void dma4(const int32_t* g, int32_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
 // The same through a buffer resource: byte `voff + soff` of the buffer
 // (per-lane and scalar parts kept apart, so that the compiler cannot turn them
 // into 64-bit per-lane pointers; reads past `bytes` return zeros).
@@ -504,6 +524,17 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   __shared__ __align__(16) uint16_t sb1[STB];
   __shared__ __align__(16) uint16_t sb2[NB == 3 ? STB : 8];
   static_assert(NA == 2, "token rows are double-buffered");
+  // Down (where the LDS has room): the row scales and output rows of the
+  // tile, loaded straight into LDS at the tile start and read by the
+  // epilogue.  Loaded by the epilogue itself, their latency stood between
+  // the last multiplication and the first store of every tile.  (The whole
+  // epilogue costs about 7 us per tile: timed without it, down on a
+  // Qwen3-235B-shaped batch took 718 instead of 915 us.)
+  constexpr bool RLDS = !GATEUP && !(BM == 256 && !F8);
+  // (one array: each array loaded straight into LDS takes a slot of the
+  // compiler's tracking of those loads, and past six it lost track and
+  // waited for every load in flight before the epilogue's LDS writes)
+  __shared__ __align__(16) int32_t s_rows[RLDS ? 2 * BM : 1];   // scale bits, then output rows
 
   // the wave index as a scalar: the weight rows a wave loads come from one
   // matrix, so their base address stays in scalar registers
@@ -516,8 +547,31 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   const int NT = ceil_div(p.ncols, HC);          // the last column tile may be partial
   const int RT2 = p2.E > 0 ? ceil_div(p2.fixed_rows, BM) : 0;
   const int T2 = RT2 * ceil_div(p2.ncols, HC);
-  const RegTiles tl = reg_tile_list<BM>(p, NT, lane);
-  const int total = T2 + tl.total;
+  // The tile list: in registers, or (PF, whose registers are tighter and
+  // whose LDS has room) in LDS.
+  constexpr bool TLDS = PF;
+  __shared__ int s_off[TLDS ? kMaxGroups + 1 : 1];
+  __shared__ int s_tp[TLDS ? kMaxGroups + 1 : 1];
+  RegTiles tl;
+  int ltotal;
+  if constexpr (TLDS) {
+    ltotal = build_tile_list<BM>(p, NT, s_off, s_tp);
+  } else {
+    tl = reg_tile_list<BM>(p, NT, lane);
+    ltotal = tl.total;
+  }
+  // group of routed tile t1: index, first tile, first row, row count
+  auto find = [&](int t1, int& e, int& first, int& base, int& cnt) {
+    if constexpr (TLDS) {
+      e = find_group(s_tp, p.E, t1);
+      first = s_tp[e];
+      base = s_off[e];
+      cnt = s_off[e + 1] - base;
+    } else {
+      reg_find(tl, t1, e, first, base, cnt);
+    }
+  };
+  const int total = T2 + ltotal;
   const int G = gridDim.x;                       // a multiple of 8
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   // Tiles come from a queue per XCD (p.queue: eight counters, zero at
@@ -596,7 +650,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     } else {
       const int t1 = t - T2;
       int first;
-      reg_find(tl, t1, e, first, base, cnt);
+      find(t1, e, first, base, cnt);
       RT = ceil_div(cnt, BM);
       local = t1 - first;
     }
@@ -626,7 +680,9 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       const int r = (BM / 8) * wave + 8 * i + lrow;
       const int ch = lslot ^ tsw(r);
       const int rr = (r < nrows) ? r : 0;
-      const int grow = q.a_rows ? q.a_rows[row0 + rr] : (row0 + rr);
+      // (down reads h in sorted order: a_rows is for gate+up only, and a load
+      // here that down never makes still cost it a wait for every load in flight)
+      const int grow = (GATEUP && q.a_rows) ? q.a_rows[row0 + rr] : (row0 + rr);
       // padding rows (past the group's count) take an offset beyond the
       // buffer: the load writes zeros and reads no memory
       if constexpr (A32) ao[i] = r < nrows ? (uint32_t)grow * (uint32_t)(2 * K) + (uint32_t)(ch * 16) : kOutOfRange;
@@ -681,7 +737,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     } else {
       const int t1 = tile - T2;
       int first;
-      reg_find(tl, t1, e, first, base, cnt);
+      find(t1, e, first, base, cnt);
       RT = ceil_div(cnt, BM);
       local = t1 - first;
     }
@@ -710,7 +766,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       const int r = (BM / 8) * wave + 8 * i + lrow;
       const int ch = lslot ^ tsw(r);
       const int rr = (r < nrows) ? r : 0;
-      const int grow = pa.a_rows ? pa.a_rows[row0 + rr] : (row0 + rr);
+      const int grow = (GATEUP && pa.a_rows) ? pa.a_rows[row0 + rr] : (row0 + rr);
       // padding rows (past the group's count) take an offset beyond the
       // buffer: the load writes zeros and reads no memory
       if constexpr (A32) aoffg[i] = r < nrows ? (uint32_t)grow * (uint32_t)(2 * K) + (uint32_t)(ch * 16) : kOutOfRange;
@@ -754,7 +810,16 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
     // the previous tile's last reads of the buffers are done
-    __syncthreads();
+    lds_barrier();
+    if constexpr (RLDS) {
+      // BM / 64 waves, one row per lane (padding rows load a live one)
+      if (wave < BM / 64) {
+        const int r = 64 * wave + lane;
+        const int rr = r < nrows ? r : 0;
+        if (pa.row_scale) dma4(reinterpret_cast<const int32_t*>(pa.row_scale) + row0 + rr, s_rows + 64 * wave);
+        if (pa.out_rows) dma4(pa.out_rows + row0 + rr, s_rows + BM + 64 * wave);
+      }
+    }
     // issue order: weights of stage 0, tokens of stage 0, then (three weight
     // buffers) the weights of stage 1; none where the previous tile loaded them
     if (!pre) {
@@ -953,12 +1018,28 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       for (int i = 0; i < NBLK; ++i) {
         const int row = wm * RB + 32 * i + fr;
         const bool in = row < nrows;
-        rsc[i] = (pa.row_scale && in) ? pa.row_scale[row0 + row] : 1.f;
-        orow_i[i] = (pa.out_rows && in) ? pa.out_rows[row0 + row] : row0 + row;
+        if constexpr (RLDS) {
+          rsc[i] = (pa.row_scale && in) ? __builtin_bit_cast(float, s_rows[row]) : 1.f;
+          orow_i[i] = (pa.out_rows && in) ? s_rows[BM + row] : row0 + row;
+        } else {
+          rsc[i] = (pa.row_scale && in) ? pa.row_scale[row0 + row] : 1.f;
+          orow_i[i] = (pa.out_rows && in) ? pa.out_rows[row0 + row] : row0 + row;
+        }
       }
-      __syncthreads();
-      uint16_t* blk = PFC ? (wave < 4 ? sa1 : sb2) + (wave & 3) * 32 * 64
-                          : (wave < 4 ? sa0 : sa1) + (wave & 3) * 32 * 64;
+      lds_barrier();
+      // Staging slots of 32 x 64 bf16 (4 KB) per wave.  PF: the next tile's
+      // first stages are in flight into sa0, sb0 and sb1, so the slots are in
+      // sb2 (free once the last stage is read) where its bf16 weight stages
+      // hold all eight (32 KB); FP8 weight stages hold four (16 KB), and the
+      // other four waves use sa1.  (A choice of two buffers leaves the
+      // compiler waiting for every load in flight before the first staging
+      // write, so bf16 keeps to one.)
+      constexpr int kSlot = 32 * 64;
+      constexpr bool STAGE_B2 = PFC && STB >= 8 * kSlot;
+      static_assert(STA >= 4 * kSlot && (NB != 3 || STB >= 4 * kSlot), "four staging slots per buffer");
+      uint16_t* blk = STAGE_B2 ? sb2 + wave * kSlot
+                    : PFC      ? (wave < 4 ? sa1 : sb2) + (wave & 3) * kSlot
+                               : (wave < 4 ? sa0 : sa1) + (wave & 3) * kSlot;
       const int c = col0 + wn * 64;
       float4 sc4[2][4];
 #pragma unroll
@@ -1060,7 +1141,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
         next = nx;                             // claimed in the last stages
       } else {
         if (tid == 0) *s_ticket = claim(tk);
-        __syncthreads();
+        lds_barrier();
         next = *s_ticket;
       }
     }
