@@ -18,16 +18,28 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bfloat16 bits, round to nearest even (NaN kept quiet).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16 bits, round to nearest even, by gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32).  A software rounding (add 0x7fff plus the
+// lowest kept bit, with a NaN test) took about a dozen instructions per value,
+// among them an exec-mask branch, in every kernel's epilogue.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// SiLU(g) * u = g / (1 + e^-g) * u, with one reciprocal instruction (about
+// 1 ulp) in place of a correctly rounded division; the product is rounded to
+// bfloat16 next.  Large negative g: e^-g = inf, the reciprocal 0, the result
+// -0 as with the division.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
+// Two floats as bfloat16 bits, lo in the low half: one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {

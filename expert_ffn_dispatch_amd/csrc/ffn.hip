@@ -286,7 +286,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void ffn_stream_kernel(FfnArgs p) 
       const int orow = row0 + r;
       if (GATEUP) {
         const float g = acc[0][i][q] * wsc[0], u = acc[1][i][q] * wsc[1];
-        p.out[(size_t)orow * ncols + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+        p.out[(size_t)orow * ncols + col] = f32_to_bf16(silu_mul(g, u));
       } else {
         const float sc = p.row_scale ? p.row_scale[orow] : 1.f;
         const size_t dst = (size_t)(p.out_rows ? p.out_rows[orow] : orow) * ncols + col;
@@ -1105,7 +1105,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float g = acc[i][0][4 * b + q] * gs[q], u = acc[i][1][4 * b + q] * us[q];
-            v[q] = g / (1.f + __expf(-g)) * u;
+            v[q] = silu_mul(g, u);
           }
           *reinterpret_cast<uint2*>(pa.out + (size_t)(row0 + row) * ncols + c) =
               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));

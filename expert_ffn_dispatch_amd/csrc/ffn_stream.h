@@ -257,7 +257,7 @@ __device__ __forceinline__ void ks_tile(const FfnArgs& p, const int* s_off, cons
       const int orow = row0 + r;
       if (GATEUP) {
         const float g = v[q] * w0s, u = v[4 + q] * w1s;
-        p.out[(size_t)orow * ncols + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+        p.out[(size_t)orow * ncols + col] = f32_to_bf16(silu_mul(g, u));
       } else {
         const float sc = p.row_scale ? p.row_scale[orow] : 1.f;
         const size_t dst = (size_t)(p.out_rows ? p.out_rows[orow] : orow) * ncols + col;
