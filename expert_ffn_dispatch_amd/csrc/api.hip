@@ -400,14 +400,19 @@ int enqueue_layer(const char* fn, const moe_dims* dims, bool ids_in, const moe_b
   }
   if (hipError_t e = mark(0)) return device_error(fn, e);
 
+  moe::PermuteArgs p{ids, A, E, k, w.counts, w.offsets, w.s2a, w.a2s, w.row_token, wts, w.row_weight,
+                     w.perm.tile_hist, w.perm.tile_off, w.queue, 4 * moe::kQueueWords};
+  // up to four tokens: the route's top-k launch (one block) also permutes
+  const bool route_perm = !ids_in && moe::route_permutes(N);
   if (!ids_in) {
     moe::RouteArgs r{x, w_router, router_bias, N, M, E, k, ids, wts};
+    if (route_perm) r.perm = &p;
     if (hipError_t e = moe::launch_route(r, w.route, st)) return device_error(fn, e);
   }
   if (hipError_t e = mark(1)) return device_error(fn, e);
-  moe::PermuteArgs p{ids, A, E, k, w.counts, w.offsets, w.s2a, w.a2s, w.row_token, wts, w.row_weight,
-                     w.perm.tile_hist, w.perm.tile_off, w.queue, 4 * moe::kQueueWords};
-  if (hipError_t e = moe::launch_permute(p, st)) return device_error(fn, e);
+  if (!route_perm) {
+    if (hipError_t e = moe::launch_permute(p, st)) return device_error(fn, e);
+  }
   if (hipError_t e = mark(2)) return device_error(fn, e);
   if (order.before != nullptr) {
     if (hipError_t e = hipStreamWaitEvent(st, order.before, 0)) return device_error(fn, e);

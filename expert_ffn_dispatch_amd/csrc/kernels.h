@@ -7,6 +7,7 @@
 
 namespace moe {
 
+struct PermuteArgs;
 struct RouteArgs {
   const uint16_t* x;         // [N][M]
   const uint16_t* w_router;  // [M][E]
@@ -14,8 +15,14 @@ struct RouteArgs {
   int N, M, E, k;
   int32_t* ids;              // [N][k]
   float* weights;            // [N][k]
+  // optional, where route_permutes(N): the dispatch and permutation of the
+  // routed ids (perm->ids and perm->weights are ids and weights), done by
+  // the top-k launch
+  const PermuteArgs* perm = nullptr;
 };
 size_t route_workspace_bytes(int N, int M, int E);
+// Batches of at most four tokens: the top-k launch (one block) also permutes.
+bool route_permutes(int N);
 hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st);
 
 // Dispatch + stable permutation.  Tiles of kPermTile assignments.

@@ -232,6 +232,91 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   rank_token<PER>(v, lane, E, k, sk[w], sx[w], ids + (size_t)n * k, wts + (size_t)n * k);
 }
 
+// At most four tokens (one block): top-k, then the dispatch and stable
+// permutation of the N*k <= 64 assignments in the same block, so the
+// decode path skips the permutation launch.  Each wave ranks one token as
+// router_topk_kernel does, into LDS; the block then stores the ids and
+// weights, counts the assignments per expert, scans the counts (one wave)
+// and places assignment a at offsets[e] plus the number of earlier
+// assignments of its expert (the order the permutation launches give).
+template <int PER>
+__global__ __launch_bounds__(256) void router_topk_tiny_kernel(const float* __restrict__ part,
+                                                               const float* __restrict__ bias, int N, int E,
+                                                               int EP, int KS, int k, int32_t* __restrict__ ids,
+                                                               float* __restrict__ wts, PermuteArgs pa) {
+  __shared__ __align__(16) uint64_t sk[4][64 * PER];
+  __shared__ float sx[4][16];
+  __shared__ int s_ids[4 * 16];
+  __shared__ float s_wts[4 * 16];
+  __shared__ int cnt[256];
+  __shared__ int off[256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (w < N) {
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      float s = 0.f;
+      if (e < E) {
+#pragma unroll 8
+        for (int ks = 0; ks < KS; ++ks) s += part[((size_t)ks * N + w) * EP + e];
+        if (bias) s += bias[e];
+      }
+      v[i] = s;
+    }
+    rank_token<PER>(v, lane, E, k, sk[w], sx[w], s_ids + w * k, s_wts + w * k);
+  }
+  if (tid < pa.n_zero) pa.zero[tid] = 0;
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+  const int A = N * k;
+  int e = 0;
+  if (tid < A) {
+    e = s_ids[tid];
+    ids[tid] = e;
+    wts[tid] = s_wts[tid];
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (w == 0) {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = lane * 4 + i;
+      c[i] = ee < E ? cnt[ee] : 0;
+      sum += c[i];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(inc, d);
+      if (lane >= d) inc += o;
+    }
+    int b = inc - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = lane * 4 + i;
+      if (ee < E) {
+        pa.counts[ee] = c[i];
+        pa.offsets[ee] = b;
+        off[ee] = b;
+      }
+      b += c[i];
+    }
+    if (lane == 63) pa.offsets[E] = inc;
+  }
+  __syncthreads();
+  if (tid < A) {
+    int r = 0;
+    for (int a2 = 0; a2 < tid; ++a2) r += s_ids[a2] == e ? 1 : 0;
+    const int pos = off[e] + r;
+    pa.s2a[pos] = tid;
+    pa.a2s[tid] = pos;
+    if (pa.row_token) pa.row_token[pos] = tid / k;
+    if (pa.row_weight) pa.row_weight[pos] = s_wts[tid];
+  }
+}
+
 // Large batches (fused_route): scores and top-k in one launch.  A block takes
 // 32 tokens and every expert (E padded to 64 * NEBW rows of the transposed
 // router) over the whole hidden dimension.  Token rows and router rows are
@@ -639,6 +724,32 @@ bool fused_route(int N, int E) {
   return !small_route(N, E) && !rows_route(N, E) && N >= kFusedMinTokens && E <= 256;
 }
 
+namespace {
+
+// Top-k over KS partial score slices of row stride EP; with a.perm (at most
+// four tokens), the permutation in the same launch.
+template <int PER>
+hipError_t launch_topk_per(const RouteArgs& a, const float* part, int EP, int KS, hipStream_t st) {
+  if (a.perm != nullptr)
+    hipLaunchKernelGGL(router_topk_tiny_kernel<PER>, dim3(1), dim3(256), 0, st, part, a.bias, a.N, a.E, EP, KS, a.k,
+                       a.ids, a.weights, *a.perm);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<PER>, dim3(ceil_div(a.N, 4)), dim3(256), 0, st, part, a.bias, a.N, a.E,
+                       EP, KS, a.k, a.ids, a.weights);
+  return hipGetLastError();
+}
+hipError_t launch_topk(const RouteArgs& a, const float* part, int EP, int KS, hipStream_t st) {
+  const int per = ceil_div(EP, 64);
+  if (per <= 1) return launch_topk_per<1>(a, part, EP, KS, st);
+  if (per <= 2) return launch_topk_per<2>(a, part, EP, KS, st);
+  if (per <= 3) return launch_topk_per<3>(a, part, EP, KS, st);
+  return launch_topk_per<4>(a, part, EP, KS, st);
+}
+
+}  // namespace
+
+bool route_permutes(int N) { return N >= 1 && N <= 4; }
+
 size_t route_workspace_bytes(int N, int M, int E) {
   if (rows_route(N, E)) {
     int slice, KS;
@@ -658,6 +769,7 @@ size_t route_workspace_bytes(int N, int M, int E) {
 
 hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
+  if (a.perm != nullptr && (!route_permutes(a.N) || a.k > 16 || a.E > 256)) return hipErrorInvalidValue;
   if (rows_route(a.N, a.E)) {
     int slice, KS;
     rows_route_plan(a.M, slice, KS);
@@ -672,14 +784,8 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
       hipLaunchKernelGGL(router_scores_rows_kernel<2>, gr, dim3(256), 0, st, a.x, a.w_router, a.N, a.M, a.E, slice, part);
     else
       hipLaunchKernelGGL(router_scores_rows_kernel<1>, gr, dim3(256), 0, st, a.x, a.w_router, a.N, a.M, a.E, slice, part);
-    const dim3 g(ceil_div(a.N, 4));
-    if (a.E <= 64)
-      hipLaunchKernelGGL(router_topk_kernel<1>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, a.E, KS, a.k, a.ids, a.weights);
-    else if (a.E <= 128)
-      hipLaunchKernelGGL(router_topk_kernel<2>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, a.E, KS, a.k, a.ids, a.weights);
-    else
-      hipLaunchKernelGGL(router_topk_kernel<4>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, a.E, KS, a.k, a.ids, a.weights);
-    return hipGetLastError();
+    if (hipError_t e = hipGetLastError()) return e;
+    return launch_topk(a, part, a.E, KS, st);
   }
   if (small_route(a.N, a.E)) {
     int slice, KS;
@@ -688,15 +794,8 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
     const size_t lds = ((size_t)kSRT * slice + 256 * kSRT) * sizeof(float);
     hipLaunchKernelGGL(router_scores_small_kernel, dim3(ceil_div(a.N, kSRT), KS), dim3(256), lds, st, a.x,
                        a.w_router, a.N, a.M, a.E, slice, part);
-    const int per = ceil_div(a.E, 64);
-    const dim3 g(ceil_div(a.N, 4));
-    if (per <= 1)
-      hipLaunchKernelGGL(router_topk_kernel<1>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, a.E, KS, a.k, a.ids, a.weights);
-    else if (per <= 2)
-      hipLaunchKernelGGL(router_topk_kernel<2>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, a.E, KS, a.k, a.ids, a.weights);
-    else
-      hipLaunchKernelGGL(router_topk_kernel<4>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, a.E, KS, a.k, a.ids, a.weights);
-    return hipGetLastError();
+    if (hipError_t e = hipGetLastError()) return e;
+    return launch_topk(a, part, a.E, KS, st);
   }
   const RoutePlan pl = plan(a.N, a.M, a.E);
   uint16_t* wt = static_cast<uint16_t*>(ws);
@@ -723,17 +822,8 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
     case 5: launch_logits<5>(a, pl, wt, part, st); break;
     default: launch_logits<4>(a, pl, wt, part, st); break;
   }
-  const int per = ceil_div(pl.EP, 64);
-  const dim3 g(ceil_div(a.N, 4));
-  if (per <= 1)
-    hipLaunchKernelGGL(router_topk_kernel<1>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
-  else if (per <= 2)
-    hipLaunchKernelGGL(router_topk_kernel<2>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
-  else if (per <= 3)
-    hipLaunchKernelGGL(router_topk_kernel<3>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
-  else
-    hipLaunchKernelGGL(router_topk_kernel<4>, g, dim3(256), 0, st, part, a.bias, a.N, a.E, pl.EP, pl.KS, a.k, a.ids, a.weights);
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  return launch_topk(a, part, pl.EP, pl.KS, st);
 }
 
 }  // namespace moe

@@ -17,6 +17,10 @@ SHAPES = [
     (64, 256, 8, 2, 512, 0, 0, False),      # the tiny workload's shape
     (37, 192, 5, 2, 320, 0, 0, False),      # ragged everything
     (1, 128, 16, 4, 128, 0, 0, False),      # one token
+    # up to four tokens: the layer's top-k launch also permutes (one block)
+    (3, 256, 256, 16, 128, 0, 0, True),     # 256 experts, top-16 (48 assignments), bias
+    (4, 128, 20, 3, 192, 1, 64, False),     # four tokens with a shared expert
+    (2, 256, 64, 8, 128, 0, 0, False),      # two tokens on the row-wise router
     (130, 320, 20, 1, 192, 0, 0, True),     # k = 1, bias
     (50, 128, 6, 6, 256, 0, 0, False),      # k = E
     (77, 256, 1, 1, 384, 0, 0, False),      # E = 1
