@@ -93,13 +93,14 @@ def test_route_rows(shape):
 
 # batches of 8192 tokens or more over more than 32 experts: scores and top-k
 # in one launch (32 tokens per block, 4-stage LDS ring over the hidden
-# dimension); ragged last blocks, hidden sizes of 1..5 stages, 48 / 160 / 256
-# padded experts (the three kernel widths)
+# dimension); ragged last blocks, hidden sizes of 1..5 and 16 stages, 48 /
+# 160 / 256 padded experts (the three kernel widths)
 FUSED_ROUTE = [
     (8204, 256, 40, 4, True),     # last block of 12 tokens, 48 padded experts
     (8192, 320, 160, 6, False),   # five stages: the ring's remainder steps
     (8192, 128, 256, 8, True),    # two stages (fewer than the ring's depth), most experts
     (8224, 64, 64, 2, False),     # one stage
+    (8200, 1024, 128, 8, True),   # sixteen stages: the ring's loop four times
 ]
 
 
