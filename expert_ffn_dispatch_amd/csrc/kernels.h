@@ -54,7 +54,8 @@ hipError_t launch_gather(const uint16_t* x, const int32_t* s2a, int k, int A, in
 // [offsets[e], offsets[e+1]) (or [0, fixed_rows) with E = 1 if fixed_rows > 0).
 struct FfnArgs {
   // phase 1 (gate+up): A rows from `a` ([rows][K]); if a_rows is set, row p
-  // of the group reads a[a_rows[p]].  phase 2 (down): A = h.
+  // of the group reads a[a_rows[p]].  phase 2 (down): A = h, in sorted order
+  // (a_rows is ignored).
   const uint16_t* a;
   const int32_t* a_rows;
   const int32_t* offsets;    // [E+1] device, or null with fixed_rows > 0
