@@ -120,6 +120,42 @@ def cpu_baseline(w, d, budget_s: float = 20.0, max_runs: int = 5):
                       f": {dt:.2f} s"}
 
 
+def dense_reference(args) -> int:
+    """hipBLASLt (torch.matmul) on dense GEMMs holding the workload's total
+    expert work: [A x M].[M x 2H] (gate+up) and [A x H].[H x M] (down), A =
+    N*k rows, both operands contraction-contiguous as the expert weights are.
+    A reference point for the grouped kernels' MFMA rate: the same flops with
+    no grouping, gathering, padding or SwiGLU.  Flushed medians, one JSON line."""
+    import statistics
+    import torch
+    from datagen import configs
+
+    w = configs.get(args.workload, args.tokens)
+    A = w.N * w.k
+    dev = torch.device("cuda:0")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    res = {"metric": "dense bf16 GEMM reference (torch.matmul / hipBLASLt)", "workload": w.title, "rows": A}
+    for name, (K, Nc) in (("gate_up", (w.M, 2 * w.H)), ("down", (w.H, w.M))):
+        a = torch.randn(A, K, device=dev).to(torch.bfloat16)
+        b = torch.randn(Nc, K, device=dev).to(torch.bfloat16)
+        a @ b.t()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(args.steps, 5)):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            a @ b.t()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = statistics.median(ts)
+        res[name] = {"shape": [A, K, Nc], "us": us, "tflops": 2.0 * A * K * Nc / us / 1e6}
+        del a, b
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def cost_model(args) -> int:
     """FinDEP's per-expert cost model (review page, section 核心公式: an expert's
     time is linear in its batch, t_e(m) = alpha_e + beta_e * m).  For each
@@ -218,6 +254,9 @@ def main() -> int:
                     help="instead of the layer: time one expert's SwiGLU FFN over per-expert batches "
                          "1..4096 at each workload's (M, H) and fit t(m) = alpha + beta*m (one JSON "
                          "line per shape)")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="instead of the layer: time hipBLASLt (torch.matmul) on dense GEMMs with the "
+                         "workload's total gate+up and down work, as a reference MFMA rate")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs one MoE layer on ONE GPU; --gpus {args.gpus} is not supported "
@@ -225,6 +264,8 @@ def main() -> int:
         return 2
     if args.cost_model:
         return cost_model(args)
+    if args.dense_reference:
+        return dense_reference(args)
 
     import torch
     import expert_ffn_dispatch_amd as moe
