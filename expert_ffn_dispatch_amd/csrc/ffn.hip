@@ -469,6 +469,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
 }
+// The same with the non-temporal hint, for weight rows that no later tile
+// reads again.
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 2);
+}
 
 // s_waitcnt for vector-memory count N only (expcnt and lgkmcnt left at their maxima)
 #define MOE_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | 0x0F70)
@@ -489,7 +494,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // pointers (more registers, used with 128-row tiles only).
 // PF: down tiles whose stage count divides by six (every segment's) load
 // the next tile's first stages in their own last two (see the stage loop).
-template <bool GATEUP, int BM, bool F8, bool A32, bool PF>
+template <bool GATEUP, int BM, bool F8, bool A32, bool PF, bool NTW = false>
 __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2) {
   constexpr int HC = GATEUP ? kTN / 2 : kTN;     // output columns per tile
   constexpr int FMW = BM / 64;                   // 32-row MFMA blocks per wave
@@ -789,11 +794,15 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
     else dma16(asrc[i] + (KT_) * kTBK, (BUF) + ldsA + 8 * i * kTBK);                              \
   }
 #define MOE_DMA_B(BUF, KT_)                                                                        \
-  _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                   \
-      dma16(wrsrc, boffg[i], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * i * (WRB / 2));
+  _Pragma("unroll") for (int i = 0; i < BI; ++i) {                                                 \
+    if constexpr (NTW) dma16_nt(wrsrc, boffg[i], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * i * (WRB / 2)); \
+    else dma16(wrsrc, boffg[i], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * i * (WRB / 2)); \
+  }
 #define MOE_DMA_B1(BUF, KT_, I_)                                                                   \
-  if constexpr ((I_) < BI)                                                                         \
-      dma16(wrsrc, boffg[I_], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * (I_) * (WRB / 2));
+  if constexpr ((I_) < BI) {                                                                       \
+    if constexpr (NTW) dma16_nt(wrsrc, boffg[I_], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * (I_) * (WRB / 2)); \
+    else dma16(wrsrc, boffg[I_], (uint32_t)((KT_) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * (I_) * (WRB / 2)); \
+  }
 
     // NBLK: this wave's 32-row blocks that hold rows of the group; the
     // others (in the group's last row tile only) are padding, whose
@@ -967,8 +976,10 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
   _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                   \
       dma16(arN, aoN[i], (uint32_t)(min((S) - KT, ktN - 1) * 2 * kTBK), (BUF) + ldsA + 8 * i * kTBK);
 #define MOE_DMA_B1N(BUF, S, I_)                                                                    \
-  if constexpr ((I_) < BI)                                                                         \
-      dma16(wrN, boN[I_], (uint32_t)(min((S) - KT, ktN - 1) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * (I_) * (WRB / 2));
+  if constexpr ((I_) < BI) {                                                                       \
+    if constexpr (NTW) dma16_nt(wrN, boN[I_], (uint32_t)(min((S) - KT, ktN - 1) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * (I_) * (WRB / 2)); \
+    else dma16(wrN, boN[I_], (uint32_t)(min((S) - KT, ktN - 1) * WRB), (BUF) + ldsB + (F8 ? 16 : 8) * (I_) * (WRB / 2)); \
+  }
       MOE_USTEPX(4, kt + 3, MOE_DMA_AC, MOE_DMA_B1N)
       MOE_USTEPX(5, kt + 4, MOE_DMA_AN, MOE_DMA_B1N)
 #undef MOE_DMA_AN
@@ -1006,7 +1017,11 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
       // 32 x 64 block at a time in a 4 KB slot of the token buffers, which
       // every wave has finished reading; 16-byte chunk c of row r sits at
       // c ^ stg_chunk(r) with its 8-byte halves swapped where stg_half(r), so
-      // neither the 8-byte writes nor the 16-byte reads conflict.  FP8: the
+      // neither the 8-byte writes nor the 16-byte reads conflict.  The rows
+      // are read once, after the launch (by the combine), so the stores carry
+      // the non-temporal hint and do not displace the weights and h rows
+      // that later tiles read again: DeepSeek-V2-shaped down 698 -> 653 us,
+      // Qwen3-235B-shaped 829 -> 822 us (flushed, one layer call).  FP8: the
       // per-channel scales of this lane's columns, four at a time.
       constexpr int RB = BM / 2;
       // the scale and output row of this lane's token rows (one per live
@@ -1072,7 +1087,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
             if (stg_half(r)) v = make_uint4(v.z, v.w, v.x, v.y);    // (t & 1: known at compile time)
             const int orow = __shfl(orow_i[i], r);
             if (wm * RB + 32 * i + r < nrows)
-              *reinterpret_cast<uint4*>(pa.out + (size_t)orow * ncols + c + ch * 8) = v;
+              __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w},
+                                          reinterpret_cast<u32x4_t*>(pa.out + (size_t)orow * ncols + c + ch * 8));
           }
         }
         __builtin_amdgcn_wave_barrier();
@@ -1157,17 +1173,27 @@ __global__ __launch_bounds__(512, 1) void ffn_tile_kernel(FfnArgs p, FfnArgs p2)
 
 template <int FM, bool GATEUP, bool F8, bool NTL, int LA = 2>
 hipError_t launch_stream_nt(const FfnArgs& a, hipStream_t st) {
-  // down: three 16-row groups per wave where the columns divide evenly and
-  // two blocks still fit a CU's LDS (at most 48 rows per pass)
+  // down: four 16-row groups per wave at 16 rows per pass, else three, where
+  // the columns divide evenly and two blocks still fit a CU's LDS.  Fewer,
+  // longer blocks pay off on short weight rows: Qwen3-30B-shaped down (1.5 KB
+  // rows) at 8 / 32 / 128 tokens took 40.0 / 74.6 / 85.0 us with two groups
+  // per wave and 39.0 / 73.0 / 81.1 us with four.
+  const bool nm4 = !GATEUP && FM == 1 && a.ncols % (4 * 4 * kSCols) == 0;
   const bool nm3 = !GATEUP && FM <= 3 && a.ncols % (4 * 3 * kSCols) == 0;
   // FP8 gate+up: eight waves per block where the columns divide evenly
   constexpr int NWG = (GATEUP && F8) ? 8 : 4;
   const bool w8 = NWG == 8 && a.ncols % (8 * kSCols) == 0;
-  const int NT = a.ncols / ((w8 ? 8 : 4) * kSCols * (GATEUP ? 1 : (nm3 ? 3 : 2)));
+  const int NT = a.ncols / ((w8 ? 8 : 4) * kSCols * (GATEUP ? 1 : (nm4 ? 4 : nm3 ? 3 : 2)));
   const long groups = a.E < a.rows_total ? a.E : a.rows_total;   // non-empty groups, at most
   const long passes = a.rows_total / (FM * 16) + groups;          // >= sum of ceil(count / rows per pass)
   const long grid = passes * NT;
   if (grid <= 0) return hipSuccess;
+  if constexpr (!GATEUP && FM == 1) {
+    if (nm4) {
+      hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP, LA, 4, F8, 4, NTL>), dim3((unsigned)grid), dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (!GATEUP && FM <= 3) {
     if (nm3) {
       hipLaunchKernelGGL((ffn_stream_kernel<FM, GATEUP, LA, 3, F8, 4, NTL>), dim3((unsigned)grid), dim3(256), 0, st, a);
@@ -1215,10 +1241,19 @@ hipError_t launch_tile_bm(const FfnArgs& a, const FfnArgs& a2, int num_cu, hipSt
   }
   // down with every segment's contraction a multiple of six 64-wide stages
   // (expert widths of 384 m, as 1536): the next-tile loads
+  // Where a typical group fits one row tile (mean rows per group <= BM), no
+  // later tile reads its weight rows again, and they are loaded with the
+  // non-temporal hint, which leaves L2 to the h rows that every column tile
+  // reads: DeepSeek-V2-shaped down (mean 154 rows, 192-row tiles) 654 ->
+  // 628 us.  Groups several tiles deep lose by it (Qwen3-235B-shaped down
+  // 830 -> 862 us), as their row tiles share each weight tile through L2.
   if constexpr (!GATEUP && A32 && BM < 256) {
     constexpr int kStages6 = 6 * kTBK;
     if (a.K % kStages6 == 0 && (a2.E == 0 || a2.K % kStages6 == 0)) {
-      hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8, A32, true>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
+      if (a.rows_total <= (long)BM * a.E)
+        hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8, A32, true, true>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
+      else
+        hipLaunchKernelGGL((ffn_tile_kernel<GATEUP, BM, F8, A32, true>), dim3((unsigned)grid), dim3(512), 0, st, a, a2);
       return hipGetLastError();
     }
   }
