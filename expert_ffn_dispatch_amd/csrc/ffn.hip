@@ -1298,12 +1298,16 @@ hipError_t launch_tile(const FfnArgs& a_in, const FfnArgs& a2_in, int num_cu, hi
 }
 
 // The split-contraction decode kernel pays off only when the plain streaming
-// launch would have too few blocks to keep every CU streaming (measured: it
-// helps a 1-token batch, and loses at 32 tokens).
+// launch would have too few blocks to keep every CU streaming.  Gate+up:
+// below 1024 blocks (measured: it helps at 1 and 8 tokens, 65 against 71 us
+// on the Qwen3-30B shape at 8, and loses at 32 tokens).  Down: below 256, one
+// per CU (Qwen3-30B shape: at 4 tokens the plain down launch takes 25.4
+// against 31.4 us, at 2 tokens 19.9 against 20.5, at 1 token 18.6 against
+// 12.2 us for the split one).
 bool use_split_waves(const FfnArgs& a, bool gateup) {
   const long groups = a.E < a.rows_total ? a.E : a.rows_total;
   const long blocks = groups * (a.ncols / (4 * kSCols * (gateup ? 1 : 2)));
-  return blocks < 1024;
+  return blocks < (gateup ? 1024 : 256);
 }
 
 template <bool GATEUP, bool F8>

@@ -25,6 +25,7 @@ CASES = [
     ("mixtral", None),
     ("dsv2", None),
     ("qwen30", 1),
+    ("qwen30", 4),
     ("qwen30", 8),
     ("qwen30", 32),
     ("qwen30", 128),
