@@ -13,16 +13,22 @@
 // scores with fp32 FMAs straight from W_r (router_scores_small_kernel), then
 // top-k; so do batches of one or two tokens over 64, 128 or 256 experts
 // (router_scores_rows_kernel, 16-byte pieces of W_r rows per thread).  Other
-// batches take three:
-//   transpose - W_r [M][E] -> W_rT [EP][M] (E padded to 16), so that both MFMA
-//               operands read 16 contiguous bytes of the contraction per lane
+// batches take two launches below 2048 tokens where E is a multiple of 8,
+// else three:
 //   logits    - one block per (16-64 tokens, up to 80 experts, k slice),
 //               its four waves splitting the slice: partial scores per slice;
 //               the contraction is split into KS slices so that even a
-//               decode batch spreads over many waves
+//               decode batch spreads over many waves.  Below 2048 tokens
+//               the router operand reads W_r as stored and turns each
+//               32-wide step around in LDS (router_logits_wr_kernel); larger
+//               batches and E % 8 != 0 read W_rT [EP][M] (E padded to 16)
+//               written by a transpose launch, so that both MFMA operands
+//               hold 8 contraction elements per lane
 //   topk      - one wave per token: sums the KS partials in slice order
 //               (deterministic), adds the bias, ranks every score against
 //               the others (ties to the lower id), renormalises the k best.
+// Batches of 8192 tokens and more take the transpose and one fused launch
+// (router_fused_kernel, below).
 #include "common.h"
 #include "kernels.h"
 
@@ -130,6 +136,123 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     if (n >= N) continue;
     const float s = red[0][v][l] + red[1][v][l] + red[2][v][l] + red[3][v][l];
     out[(size_t)n * EP + (eb0 + c) * 16 + (l & 15)] = s;
+  }
+}
+
+// The same partial scores with the router fragments taken from W_r as
+// stored ([M][E], experts fastest), so that no transpose is launched (E a
+// multiple of 8).  For each 32-wide step a wave loads the 32 x 16 NCBW block
+// of W_r it needs as 16-byte pieces (eight experts of one row), writes them
+// to a wave-private LDS tile, and reads back each lane's eight consecutive
+// contraction elements of its expert as 16-bit reads.  The next step's
+// pieces and token fragments load while the current step is multiplied.
+// Partial tiles of the four waves are added in wave order, as above.
+template <int NCBW, int RW>
+__global__ __launch_bounds__(256) void router_logits_wr_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ wr, int N, int M, int E,
+                                                               int EP, int steps_per_slice, float* __restrict__ part) {
+  constexpr int NV = RW * NCBW * 4;             // accumulator values per lane
+  constexpr int WC = NCBW * 16;                 // experts of the block
+  constexpr int PR = WC / 8;                    // 16-byte pieces per W_r row
+  constexpr int TS = WC + 8;                    // LDS tile pitch (bf16), rows 16-byte aligned
+  static_assert(32 * PR == 64 * NCBW, "NCBW pieces per lane per step");
+  union Lds {
+    float red[4][NV][64];
+    uint16_t tile[4][32 * TS];
+  };
+  __shared__ __align__(16) Lds lds;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = blockIdx.x * 16 * RW;
+  const int ks = blockIdx.y;
+  const int eb0 = blockIdx.z * NCBW;
+  const int b0 = ks * steps_per_slice;
+  const int b1 = min(M / 32, b0 + steps_per_slice);
+  const int s0 = b0 + ((b1 - b0) * wave) / 4, s1 = b0 + ((b1 - b0) * (wave + 1)) / 4;
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* xa[RW];
+#pragma unroll
+  for (int t = 0; t < RW; ++t) xa[t] = x + (size_t)min(tok0 + 16 * t + r, N - 1) * M + g * 8;
+  // piece i of this lane: row q / PR of the step, experts 8 (q % PR) .. +7, q = 64 i + lane
+  const uint16_t* wp[NCBW];
+  int wdst[NCBW];
+  bool wok[NCBW];
+#pragma unroll
+  for (int i = 0; i < NCBW; ++i) {
+    const int q = 64 * i + lane, row = q / PR, pc = q - row * PR;
+    const int e = eb0 * 16 + 8 * pc;
+    wok[i] = e < E;
+    wp[i] = wr + (size_t)row * E + (wok[i] ? e : 0);
+    wdst[i] = row * TS + 8 * pc;
+  }
+  uint16_t* tile = lds.tile[wave];
+
+  f32x4_t acc[RW][NCBW];
+#pragma unroll
+  for (int t = 0; t < RW; ++t)
+#pragma unroll
+    for (int c = 0; c < NCBW; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t pa[RW], pw[NCBW], qa[RW], qw[NCBW], bf[NCBW];
+#define MOE_WLOAD(A_, W_, S_)                                                                       \
+  {                                                                                                 \
+    _Pragma("unroll") for (int t = 0; t < RW; ++t)                                                  \
+        A_[t] = *reinterpret_cast<const u32x4_t*>(xa[t] + (S_) * 32);                               \
+    _Pragma("unroll") for (int i = 0; i < NCBW; ++i)                                                \
+        W_[i] = wok[i] ? *reinterpret_cast<const u32x4_t*>(wp[i] + (size_t)(S_) * 32 * E)           \
+                       : u32x4_t{0u, 0u, 0u, 0u};                                                   \
+  }
+  // the step's W_r block into the tile, then each lane's fragments out of it
+  // (a wave's LDS operations complete in order; the wave barriers keep the
+  // compiler from moving reads above writes or the next writes above reads)
+#define MOE_WTURN(W_)                                                                               \
+  {                                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < NCBW; ++i)                                                \
+        *reinterpret_cast<u32x4_t*>(tile + wdst[i]) = W_[i];                                        \
+    __builtin_amdgcn_wave_barrier();                                                                \
+    _Pragma("unroll") for (int c = 0; c < NCBW; ++c) {                                              \
+      const uint16_t* col = tile + (8 * g) * TS + 16 * c + r;                                       \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                 \
+          bf[c][j] = (uint32_t)col[(2 * j) * TS] | ((uint32_t)col[(2 * j + 1) * TS] << 16);         \
+    }                                                                                               \
+    __builtin_amdgcn_wave_barrier();                                                                \
+  }
+#define MOE_WMMA(A_)                                                                                \
+  _Pragma("unroll") for (int t = 0; t < RW; ++t)                                                    \
+      _Pragma("unroll") for (int c = 0; c < NCBW; ++c) acc[t][c] = mfma16(A_[t], bf[c], acc[t][c]);
+  if (s0 < s1) {
+    MOE_WLOAD(pa, pw, s0)
+    int st = s0;
+    for (; st + 1 < s1; st += 2) {
+      MOE_WLOAD(qa, qw, st + 1)
+      MOE_WTURN(pw)
+      MOE_WMMA(pa)
+      MOE_WLOAD(pa, pw, min(st + 2, s1 - 1))   // the last step re-reads itself
+      MOE_WTURN(qw)
+      MOE_WMMA(qa)
+    }
+    if (st < s1) {
+      MOE_WTURN(pw)
+      MOE_WMMA(pa)
+    }
+  }
+#undef MOE_WLOAD
+#undef MOE_WTURN
+#undef MOE_WMMA
+  __syncthreads();                               // the tiles and the partial sums share the LDS
+#pragma unroll
+  for (int t = 0; t < RW; ++t)
+#pragma unroll
+    for (int c = 0; c < NCBW; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lds.red[wave][(t * NCBW + c) * 4 + q][lane] = acc[t][c][q];
+  __syncthreads();
+  float* out = part + (size_t)ks * N * EP;
+  for (int i = threadIdx.x; i < NV * 64; i += 256) {
+    const int v = i >> 6, l = i & 63;
+    const int q = v & 3, c = (v >> 2) % NCBW, t = (v >> 2) / NCBW;
+    const int n = tok0 + 16 * t + 4 * (l >> 4) + q;
+    if (n >= N) continue;
+    const float sum = lds.red[0][v][l] + lds.red[1][v][l] + lds.red[2][v][l] + lds.red[3][v][l];
+    out[(size_t)n * EP + (eb0 + c) * 16 + (l & 15)] = sum;
   }
 }
 
@@ -691,8 +814,16 @@ RoutePlan plan(int N, int M, int E) {
 
 template <int NCBW, int RW>
 void launch_logits_rw(const RouteArgs& a, const RoutePlan& pl, const uint16_t* wt, float* part, hipStream_t st) {
-  hipLaunchKernelGGL((router_logits_kernel<NCBW, RW>), dim3(ceil_div(a.N, 16 * RW), pl.KS, pl.EG), dim3(256), 0,
-                     st, a.x, wt, a.N, a.M, pl.EP, pl.steps, part);
+  const dim3 grid(ceil_div(a.N, 16 * RW), pl.KS, pl.EG);
+  if constexpr (RW <= 2) {   // W_r as stored: batches below 2048 tokens only
+    if (wt == nullptr) {
+      hipLaunchKernelGGL((router_logits_wr_kernel<NCBW, RW>), grid, dim3(256), 0, st, a.x, a.w_router, a.N, a.M,
+                         a.E, pl.EP, pl.steps, part);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((router_logits_kernel<NCBW, RW>), grid, dim3(256), 0, st, a.x, wt, a.N, a.M, pl.EP, pl.steps,
+                     part);
 }
 
 template <int NCBW>
@@ -800,9 +931,20 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
   const RoutePlan pl = plan(a.N, a.M, a.E);
   uint16_t* wt = static_cast<uint16_t*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + (((size_t)pl.EP * a.M * 2 + 255) & ~size_t(255)));
-  hipLaunchKernelGGL(router_transpose_kernel, dim3(a.M / 64, ceil_div(pl.EP, 64)), dim3(256), 0, st, a.w_router,
-                     a.M, a.E, pl.EP, wt);
-  if (fused_route(a.N, a.E)) {
+  // Below 2048 tokens the split scores read W_r as stored where its rows
+  // hold whole 16-byte pieces of experts (E % 8 == 0): Qwen3-30B-shaped route
+  // at 8-512 tokens 17.6-19.0 -> 15.7-16.6 us, the transpose launch gone.
+  // Larger batches have many token blocks, each of which would turn the same
+  // router rows around again (DeepSeek-V2-shaped route at 4096 tokens 64 ->
+  // 73 us), and take the transpose, as do the fused launch and other E.
+  const bool fused = fused_route(a.N, a.E);
+  if (!fused && a.E % 8 == 0 && pl.RW <= 2) {
+    wt = nullptr;
+  } else {
+    hipLaunchKernelGGL(router_transpose_kernel, dim3(a.M / 64, ceil_div(pl.EP, 64)), dim3(256), 0, st, a.w_router,
+                       a.M, a.E, pl.EP, wt);
+  }
+  if (fused) {
     const dim3 g(ceil_div(a.N, 32));
     const int nebw = ceil_div(pl.EP, 64);
     if (nebw <= 2)
