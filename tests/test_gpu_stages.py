@@ -19,6 +19,8 @@ SHAPES = [
     (1, 128, 16, 4, 128, 0, 0, False),      # one token
     # up to four tokens: the layer's top-k launch also permutes (one block)
     (3, 256, 256, 16, 128, 0, 0, True),     # 256 experts, top-16 (48 assignments), bias
+    (7, 256, 64, 8, 128, 0, 0, False),      # seven tokens: router scores from W_r as stored, 64 experts
+    (8, 128, 160, 16, 128, 0, 0, True),     # the same over 160 experts (five 16-expert blocks per wave), top-16
     (4, 128, 20, 3, 192, 1, 64, False),     # four tokens with a shared expert
     (2, 256, 64, 8, 128, 0, 0, False),      # two tokens on the row-wise router
     (130, 320, 20, 1, 192, 0, 0, True),     # k = 1, bias
