@@ -18,9 +18,9 @@
 //             (lanes with the same expert and a lower lane id) plus the
 //             counts of earlier waves, so sorted slot =
 //             offsets[e] + tile_off[e][t] + rank.
-// A batch of at most kSmallPermute assignments takes one launch instead: a
-// single block counts, scans and then ranks the assignments 1024 at a time,
-// carrying each expert's running count across the chunks in LDS.
+// A batch of at most kSmallPermute assignments takes one launch instead:
+// each of its blocks counts and scans all the assignments and places its own
+// chunk of 1024 (the counts of the chunks before it give its expert bases).
 #include "common.h"
 #include "kernels.h"
 
@@ -141,44 +141,59 @@ __global__ __launch_bounds__(256) void scatter_kernel(PermuteArgs p, int T, int 
   }
 }
 
+// Up to 4096 assignments the single launch below; above, each of its blocks
+// counting every assignment costs more than the three launches (Qwen3-235B-
+// shaped batch, 65536 assignments: 29.0 against 15.5 us; DeepSeek-V2-shaped,
+// 24576: 16.1 against 14.4 us).
 constexpr int kSmallPermute = 4096;
 
-// The same dispatch and stable permutation for a small batch, in one block of
-// 16 waves: LDS histogram, one-wave scan of the counts, then chunks of 1024
-// assignments in index order, each ranked like the scatter kernel's tiles.
+// The same dispatch and stable permutation for a small batch, in one launch
+// of ceil(A / 1024) blocks of 16 waves.  Every block counts all A
+// assignments in LDS (and those of the chunks before its own), scans the
+// counts with one wave, and then ranks and places its own chunk of 1024
+// assignments like the scatter kernel's tiles: offset of the expert, plus
+// the expert's assignments in earlier chunks, in earlier waves of the chunk
+// and in lower lanes of the wave.  Counting 4096 ids again in each block is
+// cheaper than one block placing all of them: the placements are scattered
+// 4-byte stores, which one CU issues one address at a time (Qwen3-30B-shaped
+// batch of 512 tokens, 4096 assignments: 12.4 us as one block).  Block 0
+// also stores the counts and offsets and clears the tile queue words.
 __global__ __launch_bounds__(1024) void permute_small_kernel(PermuteArgs p, int nbits) {
-  constexpr int kChunks = kSmallPermute / 1024;
   __shared__ int cnt[256];
-  __shared__ int base[256];     // assignments of each expert placed by earlier chunks
+  __shared__ int base[256];     // assignments of each expert in the chunks before this block's
   __shared__ int off_s[256];
   __shared__ int wc[16][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = p.E, A = p.A;
-  if (tid < p.n_zero) p.zero[tid] = 0;
+  const int E = p.E, A = p.A, chunk = blockIdx.x;
+  if (chunk == 0 && tid < p.n_zero) p.zero[tid] = 0;
   if (tid < E) {
     cnt[tid] = 0;
     base[tid] = 0;
   }
-  // every assignment's expert (and weight) is read once, into registers
-  int ev[kChunks];
-  float wv[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int a = c * 1024 + tid;
-    ev[c] = (a < A) ? clamp_expert(p.ids[a], E) : 0;
-    wv[c] = (a < A && p.row_weight) ? p.weights[a] : 0.f;
-  }
+  for (int i = tid; i < 16 * 256; i += 1024) (&wc[0][0])[i] = 0;
+  const int a = chunk * 1024 + tid;
+  const bool valid = a < A;
+  const int e = valid ? clamp_expert(p.ids[a], E) : 0;
+  const float wv = (valid && p.row_weight) ? p.weights[a] : 0.f;
   __syncthreads();
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c)
-    if (c * 1024 + tid < A) atomicAdd(&cnt[ev[c]], 1);
+  // every assignment's expert, counted (and those of the earlier chunks)
+  const int nch = (A + 1023) >> 10;
+#pragma unroll 8
+  for (int c = 0; c < nch; ++c) {
+    const int ac = c * 1024 + tid;
+    if (ac < A) {
+      const int ec = clamp_expert(p.ids[ac], E);
+      atomicAdd(&cnt[ec], 1);
+      if (c < chunk) atomicAdd(&base[ec], 1);
+    }
+  }
   __syncthreads();
   if (wave == 0) {
     int v[4], s = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      v[i] = (e < E) ? cnt[e] : 0;
+      const int ee = lane * 4 + i;
+      v[i] = (ee < E) ? cnt[ee] : 0;
       s += v[i];
     }
     int inc = s;
@@ -190,50 +205,36 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(PermuteArgs p, int 
     int b = inc - s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane * 4 + i;
-      if (e < E) {
-        p.counts[e] = v[i];
-        p.offsets[e] = b;
-        off_s[e] = b;
+      const int ee = lane * 4 + i;
+      if (ee < E) {
+        if (chunk == 0) {
+          p.counts[ee] = v[i];
+          p.offsets[ee] = b;
+        }
+        off_s[ee] = b;
       }
       b += v[i];
     }
-    if (lane == 63) p.offsets[E] = inc;
+    if (chunk == 0 && lane == 63) p.offsets[E] = inc;
   }
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    if (c * 1024 >= A) break;   // uniform
-    for (int i = tid; i < 16 * 256; i += 1024) (&wc[0][0])[i] = 0;
-    __syncthreads();
-    const int a = c * 1024 + tid;
-    const bool valid = a < A;
-    const int e = ev[c];
-    uint64_t peers = __ballot(valid);
-    for (int bt = 0; bt < nbits; ++bt) {
-      const bool bit = (e >> bt) & 1;
-      const uint64_t m = __ballot(valid && bit);
-      peers &= bit ? m : ~m;
-    }
-    const int rank = lanes_below(peers);
-    if (valid && rank == 0) wc[wave][e] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      int before = base[e];
-      for (int w = 0; w < wave; ++w) before += wc[w][e];
-      const int pos = off_s[e] + before + rank;
-      p.s2a[pos] = a;
-      p.a2s[a] = pos;
-      if (p.row_token) p.row_token[pos] = a / p.k;
-      if (p.row_weight) p.row_weight[pos] = wv[c];
-    }
-    __syncthreads();
-    if (tid < E) {
-      int s = 0;
-#pragma unroll
-      for (int w = 0; w < 16; ++w) s += wc[w][tid];
-      base[tid] += s;
-    }
-    __syncthreads();            // wc is cleared again by the next chunk
+  // lanes of this wave with the same expert, and this lane's rank among them
+  uint64_t peers = __ballot(valid);
+  for (int bt = 0; bt < nbits; ++bt) {
+    const bool bit = (e >> bt) & 1;
+    const uint64_t m = __ballot(valid && bit);
+    peers &= bit ? m : ~m;
+  }
+  const int rank = lanes_below(peers);
+  if (valid && rank == 0) wc[wave][e] = __popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int before = base[e];
+    for (int w = 0; w < wave; ++w) before += wc[w][e];
+    const int pos = off_s[e] + before + rank;
+    p.s2a[pos] = a;
+    p.a2s[a] = pos;
+    if (p.row_token) p.row_token[pos] = a / p.k;
+    if (p.row_weight) p.row_weight[pos] = wv;
   }
 }
 
@@ -271,7 +272,8 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
   if (a.A <= kSmallPermute) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, a, nbits);
+    const int blocks = a.A > 1024 ? ceil_div(a.A, 1024) : 1;
+    hipLaunchKernelGGL(permute_small_kernel, dim3(blocks), dim3(1024), 0, st, a, nbits);
     return hipGetLastError();
   }
   if (T > 0) {
