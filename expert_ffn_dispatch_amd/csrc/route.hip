@@ -331,6 +331,83 @@ __device__ __forceinline__ void rank_token(const float (&v)[PER], int lane, int 
   __builtin_amdgcn_wave_barrier();       // sk and sx are reused for the wave's next token
 }
 
+// rank_token for NT tokens at once: every step of it is applied to the NT
+// tokens side by side (each with its own key and weight areas, sk[t] and
+// sx[t]), so that the NT dependency chains interleave (a wave ranking one
+// token at a time stalls on each compare-and-add chain: with one wave per
+// SIMD nothing else issues meanwhile).  Token t is stored only where ok[t].
+// The result of each token is the one rank_token gives.
+template <int PER, int NT>
+__device__ __forceinline__ void rank_tokens(const float (&v)[NT][PER], const bool (&ok)[NT], int lane, int E, int k,
+                                            uint64_t* const (&sk)[NT], float* const (&sx)[NT],
+                                            int32_t* const (&ids_n)[NT], float* const (&wts_n)[NT]) {
+  uint64_t key[NT][PER];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      key[t][i] = topk_key(v[t][i], e);
+      sk[t][e] = e < E ? key[t][i] : 0;    // padding loses to every expert
+    }
+  __builtin_amdgcn_wave_barrier();
+  int rank[NT][PER];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) rank[t][i] = 0;
+  for (int j = 0; j < E; j += 4) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint4 a = *reinterpret_cast<const uint4*>(&sk[t][j]);
+      const uint4 b = *reinterpret_cast<const uint4*>(&sk[t][j + 2]);
+      const uint64_t q[4] = {((uint64_t)a.y << 32) | a.x, ((uint64_t)a.w << 32) | a.z,
+                             ((uint64_t)b.y << 32) | b.x, ((uint64_t)b.w << 32) | b.z};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) rank[t][i] += q[u] > key[t][i] ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i < E && rank[t][i] < k) sx[t][rank[t][i]] = v[t][i];
+  __builtin_amdgcn_wave_barrier();
+  float ex[NT][PER];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float vmax = sx[t][0];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ex[t][i] = __expf(v[t][i] - vmax);
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i < E && rank[t][i] < k) sx[t][rank[t][i]] = ex[t][i];
+  __builtin_amdgcn_wave_barrier();
+  float sum[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) sum[t] = 0.f;
+  for (int r = 0; r < k; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sum[t] += sx[t][r];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      if (ok[t] && e < E && rank[t][i] < k) {
+        ids_n[t][rank[t][i]] = e;
+        wts_n[t][rank[t][i]] = ex[t][i] / sum[t];
+      }
+    }
+  __builtin_amdgcn_wave_barrier();       // sk and sx are reused for the wave's next tokens
+}
+
 template <int PER>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part, const float* __restrict__ bias,
                                                           int N, int E, int EP, int KS, int k,
@@ -575,18 +652,36 @@ __global__ __launch_bounds__(256, 1) void router_fused_kernel(const uint16_t* __
 #pragma unroll
       for (int q = 0; q < 4; ++q) lg[(16 * tb + 4 * fg + q) * ER + 16 * (wave + 4 * j) + fr] = acc[tb][j][q];
   __syncthreads();
-  uint64_t* sk = reinterpret_cast<uint64_t*>(s1) + wave * ER;
-  float* sx = reinterpret_cast<float*>(s2) + wave * 16;
-  for (int t = wave; t < nvalid; t += 4) {
-    float v[NEBW];
+  // RT tokens per wave at a time (t, t + 4, ...), each with its own key and
+  // weight areas
+  constexpr int RT = 4;
+  static_assert(4 * RT * ER * 8 <= ST * 2 && 4 * RT * 16 * 4 <= ST * 2, "key and weight areas fit in s1 and s2");
+  uint64_t* sk[RT];
+  float* sx[RT];
 #pragma unroll
-    for (int i = 0; i < NEBW; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = 0.f;
-      if (e < E) v[i] = lg[t * ER + e] + (bias ? bias[e] : 0.f);
+  for (int h = 0; h < RT; ++h) {
+    sk[h] = reinterpret_cast<uint64_t*>(s1) + (wave * RT + h) * ER;
+    sx[h] = reinterpret_cast<float*>(s2) + (wave * RT + h) * 16;
+  }
+  for (int t = wave; t < nvalid; t += 4 * RT) {
+    bool ok[RT];
+    float v[RT][NEBW];
+    int32_t* idp[RT];
+    float* wtp[RT];
+#pragma unroll
+    for (int h = 0; h < RT; ++h) {
+      ok[h] = t + 4 * h < nvalid;
+      const size_t n = (size_t)(n0 + (ok[h] ? t + 4 * h : t));
+      idp[h] = ids + n * k;
+      wtp[h] = wts + n * k;
+#pragma unroll
+      for (int i = 0; i < NEBW; ++i) {
+        const int e = lane + 64 * i;
+        v[h][i] = 0.f;
+        if (e < E && ok[h]) v[h][i] = lg[(t + 4 * h) * ER + e] + (bias ? bias[e] : 0.f);
+      }
     }
-    const size_t n = (size_t)(n0 + t);
-    rank_token<NEBW>(v, lane, E, k, sk, sx, ids + n * k, wts + n * k);
+    rank_tokens<NEBW, RT>(v, ok, lane, E, k, sk, sx, idp, wtp);
   }
 }
 
