@@ -25,8 +25,9 @@
 //               written by a transpose launch, so that both MFMA operands
 //               hold 8 contraction elements per lane
 //   topk      - one wave per token: sums the KS partials in slice order
-//               (deterministic), adds the bias, ranks every score against
-//               the others (ties to the lower id), renormalises the k best.
+//               (deterministic), adds the bias, takes the k best by k
+//               wave-wide maxima of order keys (ties to the lower id) and
+//               renormalises them.
 // Batches of 8192 tokens and more take the transpose and one fused launch
 // (router_fused_kernel, below).
 #include "common.h"
@@ -266,154 +267,99 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
   return ((uint64_t)m << 32) | (uint32_t)~(uint32_t)e;
 }
 
-// One wave per token.  Each lane holds PER scores (experts lane + 64 i); the
-// token's order keys are also written to this wave's LDS row, and every lane
-// counts the keys above each of its own: that count is the score's rank, and
-// ranks 0..k-1 are the k slots.  No cross-lane reduction chains: the
-// broadcast LDS reads and 64-bit compares of all lanes run side by side.
-// The weights are exp(l - l_max) of the k winners over their sum (in slot
-// order).
-// Ranks one token's scores (lane l holds experts l + 64 i in v) and writes
-// its k slots: ids in descending score order (ties to the lower id) and the
-// renormalised weights.  sk: 64 * PER keys of this wave in LDS; sx: 16 floats
-// of this wave in LDS.  Called by every lane of one wave.
-template <int PER>
-__device__ __forceinline__ void rank_token(const float (&v)[PER], int lane, int E, int k, uint64_t* sk, float* sx,
-                                           int32_t* __restrict__ ids_n, float* __restrict__ wts_n) {
-  uint64_t key[PER];
+// One lane's 64-bit value from another lane of its row of 16 (DPP pattern CTRL).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// The largest of the wave's 64 values, in every lane: within each row of 16
+// by DPP (swap within pairs, then pairs within quads, then the half-row and
+// row mirrors), then across rows by exchanges with lanes 16 and 32 away.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));      // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E>(v));      // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x141>(v));     // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140>(v));     // row_mirror
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = topk_key(v[i], e);
-    sk[e] = e < E ? key[i] : 0;          // padding loses to every expert
+  for (int d = 16; d <= 32; d *= 2) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, d);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), d);
+    v = max_u64(v, ((uint64_t)hi << 32) | lo);
   }
-  // LDS operations of a wave complete in order; the barrier only keeps the
-  // compiler from moving the reads above the writes
-  __builtin_amdgcn_wave_barrier();
-  int rank[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) rank[i] = 0;
-  // E rounded up to pairs: a padding key (0) never counts
-  for (int j = 0; j < E; j += 4) {
-    const uint4 a = *reinterpret_cast<const uint4*>(&sk[j]);
-    const uint4 b = *reinterpret_cast<const uint4*>(&sk[j + 2]);
-    const uint64_t q[4] = {((uint64_t)a.y << 32) | a.x, ((uint64_t)a.w << 32) | a.z,
-                           ((uint64_t)b.y << 32) | b.x, ((uint64_t)b.w << 32) | b.z};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) rank[i] += q[u] > key[i] ? 1 : 0;
-  }
-  // slot r of the winners: the largest score first
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (lane + 64 * i < E && rank[i] < k) sx[rank[i]] = v[i];
-  __builtin_amdgcn_wave_barrier();
-  const float vmax = sx[0];
-  float ex[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) ex[i] = __expf(v[i] - vmax);
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (lane + 64 * i < E && rank[i] < k) sx[rank[i]] = ex[i];
-  __builtin_amdgcn_wave_barrier();
-  float sum = 0.f;
-  for (int r = 0; r < k; ++r) sum += sx[r];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E && rank[i] < k) {
-      ids_n[rank[i]] = e;
-      wts_n[rank[i]] = ex[i] / sum;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();       // sk and sx are reused for the wave's next token
+  return v;
 }
 
-// rank_token for NT tokens at once: every step of it is applied to the NT
-// tokens side by side (each with its own key and weight areas, sk[t] and
-// sx[t]), so that the NT dependency chains interleave (a wave ranking one
-// token at a time stalls on each compare-and-add chain: with one wave per
-// SIMD nothing else issues meanwhile).  Token t is stored only where ok[t].
-// The result of each token is the one rank_token gives.
+// The score an order key was made from (topk_key without the id; -0 comes
+// back as +0, which changes no difference of scores below).
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t m = (uint32_t)(key >> 32);
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
+}
+
+// Ranks NT tokens' scores side by side, one wave for all of them (lane l
+// holds experts l + 64 i of token t in v[t]) and writes each token's k
+// slots: ids in descending score order (ties to the lower id) and the
+// weights exp(l_r - l_0) over their sum in slot order.  The order keys are
+// unique (their low word is the complemented expert id), so k rounds of a
+// wave-wide maximum give the slots in turn: round r's maximum is slot r's
+// winner, which is then removed, and its expert and score are read back from
+// the key.  Lane r keeps slot r.  Token t is stored only where ok[t]; the
+// interleaved tokens overlap each other's reduction chains.  No LDS; about
+// k * (PER + 30) VALU operations per token, where counting every expert's
+// rank takes E * PER 64-bit compares.  Called by every lane of one wave.
 template <int PER, int NT>
-__device__ __forceinline__ void rank_tokens(const float (&v)[NT][PER], const bool (&ok)[NT], int lane, int E, int k,
-                                            uint64_t* const (&sk)[NT], float* const (&sx)[NT],
-                                            int32_t* const (&ids_n)[NT], float* const (&wts_n)[NT]) {
+__device__ __forceinline__ void rank_tokens(const float (&v)[NT][PER], const bool (&ok)[NT], int lane, int E,
+                                                int k, int32_t* const (&ids_n)[NT], float* const (&wts_n)[NT]) {
   uint64_t key[NT][PER];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane + 64 * i;
-      key[t][i] = topk_key(v[t][i], e);
-      sk[t][e] = e < E ? key[t][i] : 0;    // padding loses to every expert
-    }
-  __builtin_amdgcn_wave_barrier();
-  int rank[NT][PER];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < PER; ++i) rank[t][i] = 0;
-  for (int j = 0; j < E; j += 4) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&sk[t][j]);
-      const uint4 b = *reinterpret_cast<const uint4*>(&sk[t][j + 2]);
-      const uint64_t q[4] = {((uint64_t)a.y << 32) | a.x, ((uint64_t)a.w << 32) | a.z,
-                             ((uint64_t)b.y << 32) | b.x, ((uint64_t)b.w << 32) | b.z};
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < PER; ++i) rank[t][i] += q[u] > key[t][i] ? 1 : 0;
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i < E && rank[t][i] < k) sx[t][rank[t][i]] = v[t][i];
-  __builtin_amdgcn_wave_barrier();
-  float ex[NT][PER];
+  float vmax[NT], sum[NT], my_ex[NT];
+  int my_e[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const float vmax = sx[t][0];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) ex[t][i] = __expf(v[t][i] - vmax);
-  }
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i < E && rank[t][i] < k) sx[t][rank[t][i]] = ex[t][i];
-  __builtin_amdgcn_wave_barrier();
-  float sum[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) sum[t] = 0.f;
-  for (int r = 0; r < k; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) sum[t] += sx[t][r];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lane + 64 * i;
-      if (ok[t] && e < E && rank[t][i] < k) {
-        ids_n[t][rank[t][i]] = e;
-        wts_n[t][rank[t][i]] = ex[t][i] / sum[t];
+      key[t][i] = e < E ? topk_key(v[t][i], e) : 0;   // 0 is below every expert's key
+    }
+    vmax[t] = 0.f;
+    sum[t] = 0.f;
+    my_ex[t] = 0.f;
+    my_e[t] = 0;
+  }
+  for (int r = 0; r < k; ++r) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint64_t m = key[t][0];
+#pragma unroll
+      for (int i = 1; i < PER; ++i) m = max_u64(m, key[t][i]);
+      m = wave_max_u64(m);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) key[t][i] = key[t][i] == m ? 0 : key[t][i];
+      const float s = key_score(m);
+      if (r == 0) vmax[t] = s;
+      const float ex = __expf(s - vmax[t]);
+      sum[t] += ex;
+      if (lane == r) {
+        my_e[t] = (int)~(uint32_t)m;
+        my_ex[t] = ex;
       }
     }
-  __builtin_amdgcn_wave_barrier();       // sk and sx are reused for the wave's next tokens
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (ok[t] && lane < k) {
+      ids_n[t][lane] = my_e[t];
+      wts_n[t][lane] = my_ex[t] / sum[t];
+    }
 }
 
 template <int PER>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part, const float* __restrict__ bias,
                                                           int N, int E, int EP, int KS, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ wts) {
-  __shared__ __align__(16) uint64_t sk[4][64 * PER];
-  __shared__ float sx[4][16];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = blockIdx.x * 4 + w;
   if (n >= N) return;                    // whole waves; no block barrier below
@@ -429,13 +375,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     }
     v[i] = s;
   }
-  rank_token<PER>(v, lane, E, k, sk[w], sx[w], ids + (size_t)n * k, wts + (size_t)n * k);
+  const float(&vt)[1][PER] = reinterpret_cast<const float(&)[1][PER]>(v);
+  int32_t* const idp[1] = {ids + (size_t)n * k};
+  float* const wtp[1] = {wts + (size_t)n * k};
+  rank_tokens<PER, 1>(vt, {true}, lane, E, k, idp, wtp);
 }
 
 // At most four tokens (one block): top-k, then the dispatch and stable
 // permutation of the N*k <= 64 assignments in the same block, so the
 // decode path skips the permutation launch.  Each wave ranks one token as
-// router_topk_kernel does, into LDS; the block then stores the ids and
+// router_topk_kernel does, its slots into LDS; the block then stores the ids and
 // weights, counts the assignments per expert, scans the counts (one wave)
 // and places assignment a at offsets[e] plus the number of earlier
 // assignments of its expert (the order the permutation launches give).
@@ -444,8 +393,6 @@ __global__ __launch_bounds__(256) void router_topk_tiny_kernel(const float* __re
                                                                const float* __restrict__ bias, int N, int E,
                                                                int EP, int KS, int k, int32_t* __restrict__ ids,
                                                                float* __restrict__ wts, PermuteArgs pa) {
-  __shared__ __align__(16) uint64_t sk[4][64 * PER];
-  __shared__ float sx[4][16];
   __shared__ int s_ids[4 * 16];
   __shared__ float s_wts[4 * 16];
   __shared__ int cnt[256];
@@ -464,7 +411,10 @@ __global__ __launch_bounds__(256) void router_topk_tiny_kernel(const float* __re
       }
       v[i] = s;
     }
-    rank_token<PER>(v, lane, E, k, sk[w], sx[w], s_ids + w * k, s_wts + w * k);
+    const float(&vt)[1][PER] = reinterpret_cast<const float(&)[1][PER]>(v);
+    int32_t* const idp[1] = {s_ids + w * k};
+    float* const wtp[1] = {s_wts + w * k};
+    rank_tokens<PER, 1>(vt, {true}, lane, E, k, idp, wtp);
   }
   if (tid < pa.n_zero) pa.zero[tid] = 0;
   if (tid < E) cnt[tid] = 0;
@@ -525,7 +475,7 @@ __global__ __launch_bounds__(256) void router_topk_tiny_kernel(const float* __re
 // on the source side, so the 16-row fragment reads are free of bank
 // conflicts); each of the four waves multiplies every fourth 16-expert block
 // against both 16-token blocks (16x16x32 MFMAs).  The scores then pass
-// through LDS to rank_token, one token at a time per wave: no partial scores
+// through LDS to rank_tokens, four tokens at a time per wave: no partial scores
 // leave the block and no second launch follows.  Against the split path
 // only the fp32 summation order of the scores differs.
 // Measured (route stage, flushed medians): Qwen3-235B-shaped router (8192
@@ -652,17 +602,8 @@ __global__ __launch_bounds__(256, 1) void router_fused_kernel(const uint16_t* __
 #pragma unroll
       for (int q = 0; q < 4; ++q) lg[(16 * tb + 4 * fg + q) * ER + 16 * (wave + 4 * j) + fr] = acc[tb][j][q];
   __syncthreads();
-  // RT tokens per wave at a time (t, t + 4, ...), each with its own key and
-  // weight areas
+  // RT tokens per wave at a time: t, t + 4, ...
   constexpr int RT = 4;
-  static_assert(4 * RT * ER * 8 <= ST * 2 && 4 * RT * 16 * 4 <= ST * 2, "key and weight areas fit in s1 and s2");
-  uint64_t* sk[RT];
-  float* sx[RT];
-#pragma unroll
-  for (int h = 0; h < RT; ++h) {
-    sk[h] = reinterpret_cast<uint64_t*>(s1) + (wave * RT + h) * ER;
-    sx[h] = reinterpret_cast<float*>(s2) + (wave * RT + h) * 16;
-  }
   for (int t = wave; t < nvalid; t += 4 * RT) {
     bool ok[RT];
     float v[RT][NEBW];
@@ -681,7 +622,7 @@ __global__ __launch_bounds__(256, 1) void router_fused_kernel(const uint16_t* __
         if (e < E && ok[h]) v[h][i] = lg[(t + 4 * h) * ER + e] + (bias ? bias[e] : 0.f);
       }
     }
-    rank_tokens<NEBW, RT>(v, ok, lane, E, k, sk, sx, idp, wtp);
+    rank_tokens<NEBW, RT>(v, ok, lane, E, k, idp, wtp);
   }
 }
 
