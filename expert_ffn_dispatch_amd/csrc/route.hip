@@ -832,8 +832,10 @@ RoutePlan plan(int N, int M, int E) {
   p.NCBW = p.NCB <= 4 ? p.NCB : p.NCB == 10 ? 5 : 4;
   p.EG = p.NCB / p.NCBW;
   // tokens per wave: more rows reuse each router fragment, fewer rows spread
-  // a small batch over more waves
-  p.RW = N >= 2048 ? 4 : (N >= 512 ? 2 : 1);
+  // a small batch over more waves.  Below 8192 tokens at most two, so that
+  // the scores can read W_r as stored: DeepSeek-V2-shaped route (4096 tokens)
+  // 59.0 -> 55.3 us against four with the transpose launch.
+  p.RW = N >= 8192 ? 4 : (N >= 512 ? 2 : 1);
   const int blocks = ceil_div(N, 16 * p.RW) * p.EG;
   const int total_steps = M / 32;
   int ks = ceil_div(1024, blocks);
@@ -851,7 +853,7 @@ RoutePlan plan(int N, int M, int E) {
 template <int NCBW, int RW>
 void launch_logits_rw(const RouteArgs& a, const RoutePlan& pl, const uint16_t* wt, float* part, hipStream_t st) {
   const dim3 grid(ceil_div(a.N, 16 * RW), pl.KS, pl.EG);
-  if constexpr (RW <= 2) {   // W_r as stored: batches below 2048 tokens only
+  if constexpr (RW <= 2) {   // W_r as stored: batches below 8192 tokens only
     if (wt == nullptr) {
       hipLaunchKernelGGL((router_logits_wr_kernel<NCBW, RW>), grid, dim3(256), 0, st, a.x, a.w_router, a.N, a.M,
                          a.E, pl.EP, pl.steps, part);
@@ -967,12 +969,13 @@ hipError_t launch_route(const RouteArgs& a, void* ws, hipStream_t st) {
   const RoutePlan pl = plan(a.N, a.M, a.E);
   uint16_t* wt = static_cast<uint16_t*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + (((size_t)pl.EP * a.M * 2 + 255) & ~size_t(255)));
-  // Below 2048 tokens the split scores read W_r as stored where its rows
+  // Below 8192 tokens the split scores read W_r as stored where its rows
   // hold whole 16-byte pieces of experts (E % 8 == 0): Qwen3-30B-shaped route
-  // at 8-512 tokens 17.6-19.0 -> 15.7-16.6 us, the transpose launch gone.
-  // Larger batches have many token blocks, each of which would turn the same
-  // router rows around again (DeepSeek-V2-shaped route at 4096 tokens 64 ->
-  // 73 us), and take the transpose, as do the fused launch and other E.
+  // at 8-512 tokens 17.6-19.0 -> 15.7-16.6 us, the transpose launch gone;
+  // DeepSeek-V2-shaped at 4096 tokens, two token blocks per wave, 59.0 ->
+  // 55.3 us (with four per wave, each block turning the same router rows
+  // around, it had been 64 -> 73 us).  The fused launch and other E take
+  // the transpose.
   const bool fused = fused_route(a.N, a.E);
   if (!fused && a.E % 8 == 0 && pl.RW <= 2) {
     wt = nullptr;
